@@ -1,0 +1,50 @@
+"""Compile libattn_decode.so (gfx950) in-tree with hipcc.
+
+Sources: csrc/attn_host.cpp (host-only planning and checks) and
+csrc/attn_decode.hip (kernels and launchers).  Packed-fp32 VALU ops are
+disabled for device code.
+"""
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+LIB = os.path.join(PKG, "libattn_decode.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-I" + os.path.join(ROOT, "include"),
+          "--offload-arch=" + ARCH]
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError("build failed:\n" + out)
+    if verbose and out.strip():
+        print(out, flush=True)
+
+
+def build(verbose: bool = True) -> str:
+    bdir = os.path.join(ROOT, "_build")
+    os.makedirs(bdir, exist_ok=True)
+    objs = []
+    for src in ("attn_host.cpp", "attn_decode.hip"):
+        obj = os.path.join(bdir, src + ".o")
+        lang = ["-x", "hip"] if src.endswith(".hip") else []
+        _run([HIPCC] + COMMON + DEVICE_FLAGS + lang + ["-c", os.path.join(PKG, "csrc", src),
+                                                       "-o", obj], verbose)
+        objs.append(obj)
+    tmp = LIB + ".tmp"
+    _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs, verbose)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose="-q" not in sys.argv)

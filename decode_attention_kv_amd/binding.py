@@ -1,0 +1,245 @@
+"""ctypes binding of libattn_decode.so (declared in include/attn_decode.h).
+
+Argument marshalling only: every step of the decode (planning, paged
+gather, scores, softmax, P.V, split merge) runs inside the native library.
+The functions named like the C entry points take raw pointers and sizes;
+``decode`` below accepts torch tensors, builds the descriptor and plan,
+allocates the workspace with torch (plumbing) and calls them.  There is no
+fallback: if the library is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, Structure, c_char_p, c_float, c_int, c_int32, c_int64, c_size_t, c_void_p
+from typing import Optional
+
+import numpy as np
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn_decode.so")
+
+ATTN_OK = 0
+ATTN_ERR_INVALID_ARG = -1
+ATTN_ERR_UNSUPPORTED = -2
+ATTN_ERR_WORKSPACE = -3
+ATTN_ERR_HIP = -4
+ATTN_FP32 = 0
+ATTN_BF16 = 1
+TILE = 64
+
+
+class PagedKV(Structure):
+    _fields_ = [("pool0", c_void_p), ("pool1", c_void_p), ("rope_pool", c_void_p),
+                ("page_table", c_void_p), ("seqlens", c_void_p), ("batch", c_int32),
+                ("max_pages_per_seq", c_int32), ("page_size", c_int32), ("num_pages", c_int32),
+                ("page_stride", c_int64), ("token_stride", c_int64), ("head_stride", c_int64),
+                ("rope_page_stride", c_int64), ("rope_token_stride", c_int64),
+                ("rope_head_stride", c_int64), ("dtype", c_int)]
+
+
+class Plan(Structure):
+    _fields_ = [("n_items", c_int32), ("batch", c_int32), ("n_groups", c_int32),
+                ("q_len", c_int32), ("max_splits", c_int32), ("n_partial_slots", c_int32),
+                ("items", c_void_p), ("seqinfo", c_void_p)]
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {attn_status_string(status)} ({status})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """Load the native library once; raise if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+    L = ctypes.CDLL(LIB_PATH)
+    L.attn_status_string.argtypes = [c_int]
+    L.attn_status_string.restype = c_char_p
+    L.attn_decode_plan_max_items.argtypes = [c_int, c_int, c_int]
+    L.attn_decode_plan_max_items.restype = c_int
+    L.attn_decode_plan.argtypes = [c_void_p, c_int, c_int, c_int, c_int, c_int, c_int, c_int,
+                                   c_int, c_int, c_void_p, c_void_p, c_int, POINTER(Plan)]
+    L.attn_decode_plan.restype = c_int
+    L.attn_decode_workspace_size.argtypes = [POINTER(Plan), c_int, c_int]
+    L.attn_decode_workspace_size.restype = c_size_t
+    common_tail = [c_float, c_int, POINTER(Plan), c_void_p, c_size_t, c_void_p]
+    L.attn_decode_gqa.argtypes = ([POINTER(PagedKV), c_void_p, c_void_p, c_void_p, c_int, c_int,
+                                   c_int, c_int] + common_tail)
+    L.attn_decode_gqa.restype = c_int
+    L.attn_decode_gta.argtypes = ([POINTER(PagedKV), c_void_p, c_void_p, c_void_p, c_int, c_int,
+                                   c_int, c_int, c_int, c_int, c_float] + common_tail)
+    L.attn_decode_gta.restype = c_int
+    L.attn_decode_latent.argtypes = ([POINTER(PagedKV), c_void_p, c_void_p, c_void_p, c_int, c_int,
+                                      c_int, c_int, c_int] + common_tail)
+    L.attn_decode_latent.restype = c_int
+    L.attn_paged_kv_check.argtypes = [POINTER(PagedKV)]
+    L.attn_paged_kv_check.restype = c_int
+    _lib = L
+    return L
+
+
+# ------------------------------------------------------------ C entry points
+def attn_status_string(status: int) -> str:
+    return lib().attn_status_string(int(status)).decode()
+
+
+def attn_decode_plan_max_items(batch: int, n_groups: int, max_seqlen: int) -> int:
+    return lib().attn_decode_plan_max_items(batch, n_groups, max_seqlen)
+
+
+def attn_decode_plan(seqlens_host: np.ndarray, batch: int, q_len: int, h_q: int, n_groups: int,
+                     token_bytes: int, d_v: int, cu_count: int, chunk_tokens: int, causal: int,
+                     items_host: np.ndarray, seqinfo_host: np.ndarray, max_items: int):
+    """Returns (status, Plan).  Host numpy arrays, int32, C-contiguous."""
+    for a in (seqlens_host, items_host, seqinfo_host):
+        assert a.dtype == np.int32 and a.flags.c_contiguous
+    plan = Plan()
+    st = lib().attn_decode_plan(seqlens_host.ctypes.data, batch, q_len, h_q, n_groups,
+                                token_bytes, d_v, cu_count, chunk_tokens, int(causal),
+                                items_host.ctypes.data, seqinfo_host.ctypes.data, max_items,
+                                ctypes.byref(plan))
+    return st, plan
+
+
+def attn_decode_workspace_size(plan: Plan, h_q: int, d_v: int) -> int:
+    return lib().attn_decode_workspace_size(ctypes.byref(plan), h_q, d_v)
+
+
+def attn_decode_gqa(kv, q, out, lse, q_len, h_q, h_kv, d, scale, causal, plan, ws, ws_bytes,
+                    stream) -> int:
+    return lib().attn_decode_gqa(ctypes.byref(kv), q, out, lse, q_len, h_q, h_kv, d, scale,
+                                 causal, ctypes.byref(plan), ws, ws_bytes, stream)
+
+
+def attn_decode_gta(kv, q, out, lse, q_len, h_q, h_kv, d, d_rope, n_rope_heads, rope_theta,
+                    scale, causal, plan, ws, ws_bytes, stream) -> int:
+    return lib().attn_decode_gta(ctypes.byref(kv), q, out, lse, q_len, h_q, h_kv, d, d_rope,
+                                 n_rope_heads, rope_theta, scale, causal, ctypes.byref(plan), ws,
+                                 ws_bytes, stream)
+
+
+def attn_decode_latent(kv, q, out, lse, q_len, h_q, h_c, d_c, d_rope, scale, causal, plan, ws,
+                       ws_bytes, stream) -> int:
+    return lib().attn_decode_latent(ctypes.byref(kv), q, out, lse, q_len, h_q, h_c, d_c, d_rope,
+                                    scale, causal, ctypes.byref(plan), ws, ws_bytes, stream)
+
+
+def attn_paged_kv_check(kv: PagedKV) -> int:
+    return lib().attn_paged_kv_check(ctypes.byref(kv))
+
+
+# ------------------------------------------------------------ torch plumbing
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def paged_kv(pool0, pool1, rope, page_table, seqlens) -> PagedKV:
+    """Descriptor over torch tensors pool [pages, P, heads, width] (any strides
+    whose innermost stride is 1), page_table int32 [B, max_pages], seqlens
+    int32 [B].  Works for host tensors too (for attn_paged_kv_check)."""
+    import torch
+
+    if pool0.stride(-1) != 1 or (pool1 is not None and pool1.stride(-1) != 1):
+        raise ValueError("pool rows must be contiguous")
+    kv = PagedKV()
+    kv.pool0, kv.pool1, kv.rope_pool = _ptr(pool0), _ptr(pool1), _ptr(rope)
+    kv.page_table, kv.seqlens = page_table.data_ptr(), seqlens.data_ptr()
+    kv.batch = page_table.shape[0]
+    kv.max_pages_per_seq = page_table.shape[1]
+    kv.page_size = pool0.shape[1]
+    kv.num_pages = pool0.shape[0]
+    kv.page_stride, kv.token_stride, kv.head_stride = pool0.stride(0), pool0.stride(1), pool0.stride(2)
+    if rope is not None:
+        kv.rope_page_stride, kv.rope_token_stride, kv.rope_head_stride = (
+            rope.stride(0), rope.stride(1), rope.stride(2))
+    if pool0.dtype == torch.bfloat16:
+        kv.dtype = ATTN_BF16
+    elif pool0.dtype == torch.float32:
+        kv.dtype = ATTN_FP32
+    else:
+        raise ValueError(f"unsupported dtype {pool0.dtype}")
+    return kv
+
+
+class DevicePlan:
+    """A host plan plus its device copy (keeps the device arrays alive)."""
+
+    def __init__(self, seqlens_host, q_len, h_q, n_groups, token_bytes, d_v, device,
+                 cu_count=256, chunk_tokens=0, causal=False):
+        import torch
+
+        seqlens_host = np.ascontiguousarray(seqlens_host, dtype=np.int32)
+        batch = len(seqlens_host)
+        max_items = attn_decode_plan_max_items(batch, n_groups, int(max(1, seqlens_host.max(initial=0))))
+        if max_items < 0:
+            raise AttnError(max_items, "attn_decode_plan_max_items")
+        self.items_host = np.zeros((max_items, 4), dtype=np.int32)
+        self.seqinfo_host = np.zeros((batch, 4), dtype=np.int32)
+        st, plan = attn_decode_plan(seqlens_host, batch, q_len, h_q, n_groups, token_bytes, d_v,
+                                    cu_count, chunk_tokens, int(causal), self.items_host,
+                                    self.seqinfo_host, max_items)
+        if st != ATTN_OK:
+            raise AttnError(st, "attn_decode_plan")
+        self.items_dev = torch.from_numpy(self.items_host[:plan.n_items].copy()).to(device)
+        self.seqinfo_dev = torch.from_numpy(self.seqinfo_host).to(device)
+        plan.items = self.items_dev.data_ptr()
+        plan.seqinfo = self.seqinfo_dev.data_ptr()
+        self.plan = plan
+
+
+def token_bytes(kind: str, head_dim: int, d_rope: int, elem: int) -> int:
+    if kind == "gqa":
+        return 2 * head_dim * elem
+    return (head_dim + d_rope) * elem
+
+
+def decode(kind: str, q, pool0, pool1, rope, page_table, seqlens, seqlens_host, *, groups: int,
+           scale: float, causal: bool = False, rope_theta: float = 0.0, d_rope: int = 0,
+           out=None, lse=None, chunk_tokens: int = 0, cu_count: int = 256, plan=None,
+           workspace=None, stream=None):
+    """Run one decode through the native library on torch tensors.
+
+    kind: "gqa" | "gta" | "latent".  q [B, T, H, Dq]; pools as in the header.
+    Returns (out, lse, plan, workspace) so callers can reuse plan/workspace.
+    """
+    import torch
+
+    B, T, H, _ = q.shape
+    width = pool0.shape[-1]
+    d_v = width
+    elem = pool0.element_size()
+    if plan is None:
+        plan = DevicePlan(seqlens_host, T, H, groups, token_bytes(kind, width, d_rope, elem), d_v,
+                          q.device, cu_count=cu_count, chunk_tokens=chunk_tokens, causal=causal)
+    need = attn_decode_workspace_size(plan.plan, H, d_v)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, T, H, d_v), dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, T, H), dtype=torch.float32, device=q.device)
+    kv = paged_kv(pool0, pool1, rope, page_table, seqlens)
+    s = (stream if stream is not None else torch.cuda.current_stream(q.device)).cuda_stream
+    if kind == "gqa":
+        st = attn_decode_gqa(kv, q.data_ptr(), out.data_ptr(), lse.data_ptr(), T, H, groups, width,
+                             scale, int(causal), plan.plan, workspace.data_ptr(), need, s)
+    elif kind == "gta":
+        st = attn_decode_gta(kv, q.data_ptr(), out.data_ptr(), lse.data_ptr(), T, H, groups, width,
+                             d_rope, 1, rope_theta, scale, int(causal), plan.plan,
+                             workspace.data_ptr(), need, s)
+    elif kind == "latent":
+        st = attn_decode_latent(kv, q.data_ptr(), out.data_ptr(), lse.data_ptr(), T, H, groups,
+                                width, d_rope, scale, int(causal), plan.plan,
+                                workspace.data_ptr(), need, s)
+    else:
+        raise ValueError(kind)
+    if st != ATTN_OK:
+        raise AttnError(st, f"attn_decode_{kind}")
+    return out, lse, plan, workspace

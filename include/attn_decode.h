@@ -1,0 +1,212 @@
+/*
+ * attn_decode.h - C ABI of the MI355X (gfx950) paged-KV decode-attention
+ * library libattn_decode.so.
+ *
+ * What it computes.  For every query row r = (b, t, h) of a decode step with
+ * q_len = T query tokens per sequence, the scaled dot-product softmax
+ * attention over the keys of sequence b that the row sees:
+ *
+ *     s_i = scale * <q'_r, k_i>,   p = softmax(s),   o_r = sum_i p_i v_i,
+ *     lse_r = ln sum_i exp(s_i)            (natural log, scale included)
+ *
+ * Key i of a sequence of length L sits at position i; query t sits at
+ * position L - T + t; with causal masking (T > 1, speculative verification,
+ * "Hardware-Efficient Attention for Fast Decoding", "If this is right") row
+ * t sees keys i <= L - T + t, otherwise all L keys.  Query head h uses group
+ * j = floor(h / g), g = h_q / groups (grouped-query attention as summarised
+ * on "The Gist Talk" podcast page).  The three variants differ in what the
+ * cache holds per token and how k, v and q' are formed
+ * ("Hardware-Efficient Attention for Fast Decoding", "What carries the
+ * argument", "Core claim", Figure 2 caption):
+ *
+ *   GQA    : k = K[j], v = V[j], q' = q                       (separate K, V)
+ *   GTA    : k = [S[j][0 : d-d_r] || RoPE(R, i)], v = S[j],
+ *            q' = [q[0 : d-d_r] || RoPE(q[d-d_r : d], L-T+t)] (tied state S,
+ *            one RoPE head R broadcast to every group)
+ *   latent : k = [C[j] || R], v = C[j], q' = q                (MLA: 1 latent
+ *            head; GLA: h_c heads; q is the weight-absorbed query whose last
+ *            d_r entries are already rotated; output is d_c wide)
+ *
+ * RoPE pairs element k with element k + d_r/2 and rotates the pair by the
+ * angle pos * theta^(-2k/d_r).
+ *
+ * Method.  Split-KV decoding: a host-side plan cuts every sequence into
+ * chunks (work items); one kernel computes, per item, the online-softmax
+ * attention over its chunk; a second kernel merges the chunks of a sequence
+ * through their softmax denominators (the decomposition noted for Hydragen
+ * on the "Efficient Inference" tag page).
+ *
+ * Memory and ownership.  Every pointer passed to a decode call is DEVICE
+ * memory owned by the caller (except where marked host).  The library never
+ * allocates, frees or synchronises; all GPU work is enqueued on the given
+ * stream and ATTN_OK means "enqueued".  Arguments are validated on the host
+ * before anything is enqueued; a negative status means nothing was launched.
+ * The library keeps no state and is reentrant.
+ */
+#ifndef ATTN_DECODE_H
+#define ATTN_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARG = -1, /* null pointer, bad size, inconsistent shapes     */
+  ATTN_ERR_UNSUPPORTED = -2, /* valid but not compiled in (head dims, dtype...)  */
+  ATTN_ERR_WORKSPACE = -3,   /* workspace / plan buffer too small               */
+  ATTN_ERR_HIP = -4          /* a HIP launch reported an error                  */
+} attn_status_t;
+
+typedef enum { ATTN_FP32 = 0, ATTN_BF16 = 1 } attn_dtype_t;
+
+/*
+ * Paged KV cache descriptor ("Hardware-Efficient Attention for Fast
+ * Decoding", "If this is right": paged KV with a per-sequence page table).
+ *
+ * Logical token i of sequence b lives in physical page
+ * page_table[b * max_pages_per_seq + i / page_size], slot i % page_size.
+ * Element (page, slot, head, e) of pool0/pool1 is at
+ *     page * page_stride + slot * token_stride + head * head_stride + e
+ * and of rope_pool at the rope_* strides (strides in ELEMENTS).  The default
+ * layout is [num_pages][page_size][heads][width] row-major.
+ *
+ *   pool0     GQA: K pool | GTA: tied-state pool | latent: latent pool
+ *   pool1     GQA: V pool | otherwise NULL
+ *   rope_pool GTA: un-rotated single-head RoPE key | latent: rotated RoPE key
+ *             | GQA: NULL
+ *   page_table int32 [batch][max_pages_per_seq]; entries for pages a
+ *             sequence uses are in [0, num_pages); the rest may be -1 and are
+ *             never read.
+ *   seqlens   int32 [batch], 0 <= seqlens[b] <= max_pages_per_seq*page_size.
+ *
+ * Requirements: page_size is a power of two; pool base pointers and every
+ * row start are 16-byte aligned (strides * element size multiple of 16).
+ * Slots past a sequence's length and pages no sequence uses are never read,
+ * so they may hold anything (NaN included).
+ */
+typedef struct {
+  const void* pool0;
+  const void* pool1;
+  const void* rope_pool;
+  const int32_t* page_table;
+  const int32_t* seqlens;
+  int32_t batch;
+  int32_t max_pages_per_seq;
+  int32_t page_size;
+  int32_t num_pages;
+  int64_t page_stride, token_stride, head_stride;
+  int64_t rope_page_stride, rope_token_stride, rope_head_stride;
+  attn_dtype_t dtype;
+} attn_paged_kv_t;
+
+/*
+ * Split plan: which (sequence, group, token chunk) each workgroup handles.
+ * Filled on the host by attn_decode_plan; the caller copies the two host
+ * arrays to device memory and stores the device pointers in `items` and
+ * `seqinfo` before the decode call.
+ *
+ *   items   [n_items][4]  int32: b, group j, split index s, first token t0
+ *           (the chunk is [t0, min(t0 + chunk, L_b)))
+ *   seqinfo [batch][4]    int32: n_splits_b, partial slot base, L_b, chunk
+ */
+typedef struct {
+  int32_t n_items;
+  int32_t batch;
+  int32_t n_groups;
+  int32_t q_len;
+  int32_t max_splits;      /* largest n_splits_b                                 */
+  int32_t n_partial_slots; /* sum of n_splits_b over sequences with n_splits_b>1 */
+  const int32_t* items;    /* DEVICE copy of items_host                          */
+  const int32_t* seqinfo;  /* DEVICE copy of seqinfo_host                        */
+} attn_plan_t;
+
+/* Upper bound on the work items attn_decode_plan can emit (host-only). */
+int attn_decode_plan_max_items(int batch, int n_groups, int max_seqlen);
+
+/*
+ * Build a split plan on the host (integer work only, no GPU calls).
+ *   seqlens_host  host int32 [batch]
+ *   q_len, h_q    query tokens per sequence and query heads
+ *   n_groups      KV heads (GQA/GTA) or latent heads h_c (latent)
+ *   token_bytes   cache bytes one group's work item reads per token
+ *                 (GQA 2*d*elem, GTA (d+d_rope)*2, latent (d_c+d_rope)*2)
+ *   d_v           output width per head (sizes the split partials)
+ *   cu_count      compute units of the target GPU (256 on MI355X)
+ *   chunk_tokens  0: automatic split (balances the longest chunk against
+ *                 the partial-result traffic that more splits cost);
+ *                 > 0: force chunks of this many tokens (multiple of 64)
+ *   causal        nonzero: every seqlen must be >= q_len
+ *   items_host    host int32 [max_items][4], seqinfo_host host int32 [batch][4]
+ * Errors: INVALID_ARG for null pointers, non-positive sizes, negative
+ * lengths, causal lengths below q_len, chunk_tokens not a multiple of 64;
+ * WORKSPACE if max_items is too small.  On success plan->items and
+ * plan->seqinfo are NULL; the caller sets them to the device copies.
+ */
+int attn_decode_plan(const int32_t* seqlens_host, int batch, int q_len, int h_q,
+                     int n_groups, int token_bytes, int d_v, int cu_count,
+                     int chunk_tokens, int causal, int32_t* items_host,
+                     int32_t* seqinfo_host, int max_items, attn_plan_t* plan);
+
+/*
+ * Bytes of device workspace a decode call needs for split partials:
+ * fp32 O_part [slots][q_len][h_q][d_v] followed by fp32 LSE_part
+ * [slots][q_len][h_q], slots = plan->n_partial_slots (0 if nothing splits).
+ */
+size_t attn_decode_workspace_size(const attn_plan_t* plan, int h_q, int d_v);
+
+/*
+ * GQA decode (GTA/MQA/MHA-compatible layout with separate K and V pools).
+ *   q    [batch][q_len][h_q][d]       dtype of kv->dtype, contiguous
+ *   out  [batch][q_len][h_q][d]       same dtype, contiguous
+ *   lse  [batch][q_len][h_q] fp32, or NULL
+ * Supported: d in {64, 128}; h_q % h_kv == 0; q_len in [1, 16].
+ */
+int attn_decode_gqa(const attn_paged_kv_t* kv, const void* q, void* out, float* lse,
+                    int q_len, int h_q, int h_kv, int d, float softmax_scale, int causal,
+                    const attn_plan_t* plan, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream);
+
+/*
+ * GTA decode: tied state pool0 [.., h_kv, d], single-head RoPE key
+ * rope_pool [.., n_rope_heads = 1, d_rope].  With rope_theta > 0 the key's
+ * RoPE slice and the query's last d_rope entries are rotated in the kernel;
+ * with rope_theta <= 0 both are taken as already rotated.
+ *   q [batch][q_len][h_q][d], out [batch][q_len][h_q][d], lse as for GQA.
+ * Supported: bf16, d = 128, d_rope = 64, n_rope_heads = 1.
+ */
+int attn_decode_gta(const attn_paged_kv_t* kv, const void* q, void* out, float* lse,
+                    int q_len, int h_q, int h_kv, int d, int d_rope, int n_rope_heads,
+                    float rope_theta, float softmax_scale, int causal,
+                    const attn_plan_t* plan, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream);
+
+/*
+ * Latent decode (MLA: h_c = 1, GLA: h_c > 1) in the weight-absorbed space.
+ *   q   [batch][q_len][h_q][d_c + d_rope] (RoPE part already rotated)
+ *   out [batch][q_len][h_q][d_c]
+ * Supported: bf16, (d_c, d_rope) in {(512, 64), (256, 64)}, h_q % h_c == 0.
+ */
+int attn_decode_latent(const attn_paged_kv_t* kv, const void* q, void* out, float* lse,
+                       int q_len, int h_q, int h_c, int d_c, int d_rope,
+                       float softmax_scale, int causal, const attn_plan_t* plan,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Host-side consistency check of a descriptor whose page_table and seqlens
+ * point to HOST copies: every page a sequence uses is in [0, num_pages) and
+ * every length fits the page table.  Returns ATTN_OK or INVALID_ARG.
+ */
+int attn_paged_kv_check(const attn_paged_kv_t* host_copy);
+
+/* Static description of a status code. */
+const char* attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ATTN_DECODE_H */

@@ -1,0 +1,208 @@
+"""The C ABI on the host: the library loads, exports every declared entry
+point, and its host-only logic (planning, workspace sizing, descriptor
+checks, argument validation) behaves as the header states.  No GPU needed:
+every call here returns before anything is enqueued."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from decode_attention_kv_amd import binding
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "attn_decode.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(attn_[a-z_0-9]+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 8, names
+    lib = binding.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    assert binding.attn_status_string(0) == "ok"
+    for s in (-1, -2, -3, -4):
+        assert binding.attn_status_string(s) not in ("ok", "unknown status")
+    assert binding.attn_status_string(12345) == "unknown status"
+
+
+def _plan(seqlens, q_len=1, h_q=32, groups=8, tb=512, d_v=128, cu=256, chunk=0, causal=0):
+    seqlens = np.asarray(seqlens, dtype=np.int32)
+    mi = binding.attn_decode_plan_max_items(len(seqlens), groups, int(max(1, seqlens.max())))
+    items = np.zeros((mi, 4), np.int32)
+    info = np.zeros((len(seqlens), 4), np.int32)
+    st, plan = binding.attn_decode_plan(seqlens, len(seqlens), q_len, h_q, groups, tb, d_v, cu,
+                                        chunk, causal, items, info, mi)
+    return st, plan, items[:max(plan.n_items, 0)], info
+
+
+@pytest.mark.parametrize("chunk", [0, 64, 320])
+def test_plan_covers_every_token_once(chunk):
+    rng = np.random.default_rng(3)
+    seqlens = rng.integers(0, 5000, size=37).astype(np.int32)
+    seqlens[5] = 0
+    st, plan, items, info = _plan(seqlens, chunk=chunk)
+    assert st == 0
+    G = 8
+    cover = {}
+    for b, j, s, t0 in items.tolist():
+        n, base, L, ch = info[b]
+        assert L == seqlens[b] and 0 <= s < n and t0 == s * ch and ch % 64 == 0
+        cover.setdefault((b, j), []).append((t0, min(t0 + ch, L)))
+    for b, L in enumerate(seqlens.tolist()):
+        for j in range(G):
+            spans = sorted(cover[(b, j)])
+            assert spans[0][0] == 0 and spans[-1][1] == L
+            for (a0, a1), (b0, b1) in zip(spans, spans[1:]):
+                assert a1 == b0 and a0 < a1
+    # partial slots: contiguous, one per split of every split sequence
+    slots = [(info[b, 1], info[b, 0]) for b in range(len(seqlens)) if info[b, 0] > 1]
+    assert sum(n for _, n in slots) == plan.n_partial_slots
+    nxt = 0
+    for base, n in slots:
+        assert base == nxt
+        nxt += n
+    assert all(info[b, 1] == -1 for b in range(len(seqlens)) if info[b, 0] == 1)
+    assert plan.max_splits == info[:, 0].max()
+    if chunk:
+        assert (info[:, 3] == chunk).all()
+
+
+def test_plan_is_deterministic_and_longest_first():
+    seqlens = np.array([100, 8000, 3000, 64], np.int32)
+    a = _plan(seqlens)
+    b = _plan(seqlens)
+    assert np.array_equal(a[2], b[2]) and np.array_equal(a[3], b[3])
+    items, info = a[2], a[3]
+    lens = [min(t0 + info[b_, 3], info[b_, 2]) - t0 for b_, _, _, t0 in items.tolist()]
+    full = [l == info[b_, 3] for (b_, _, _, _), l in zip(items.tolist(), lens)]
+    # all full-length chunks come before any shorter tail chunk
+    assert full == sorted(full, reverse=True)
+
+
+def test_plan_auto_split_balances_load():
+    # one long sequence must be split so its chunks do not dominate
+    seqlens = np.array([131072] * 16, np.int32)
+    st, plan, items, info = _plan(seqlens, q_len=4, h_q=128, groups=2, tb=640, d_v=256)
+    assert st == 0 and plan.max_splits > 1
+    # partial traffic stays a small fraction of the cache bytes
+    part = plan.n_partial_slots * 4 * 128 * (256 + 1) * 4 * 2
+    kv = int(seqlens.sum()) * 1152
+    assert part < 0.1 * kv
+    # a short uniform batch that already fills the GPU is not split
+    st, plan, _, _ = _plan(np.full(512, 256, np.int32), groups=8)
+    assert plan.max_splits == 1
+
+
+def test_plan_errors():
+    assert _plan([10, 20], chunk=100)[0] == binding.ATTN_ERR_INVALID_ARG
+    assert _plan([10, -1])[0] == binding.ATTN_ERR_INVALID_ARG
+    assert _plan([2, 20], q_len=4, causal=1)[0] == binding.ATTN_ERR_INVALID_ARG
+    assert _plan([10, 20], h_q=30, groups=8)[0] == binding.ATTN_ERR_INVALID_ARG
+    seq = np.array([5000], np.int32)
+    items = np.zeros((2, 4), np.int32)
+    info = np.zeros((1, 4), np.int32)
+    st, _ = binding.attn_decode_plan(seq, 1, 1, 32, 8, 512, 128, 256, 64, 0, items, info, 2)
+    assert st == binding.ATTN_ERR_WORKSPACE
+
+
+def test_workspace_size():
+    st, plan, _, info = _plan([5000, 100], chunk=64)
+    slots = int(info[info[:, 0] > 1, 0].sum())
+    rows = slots * 1 * 32
+    expect = (rows * 128 * 4 + 255) // 256 * 256 + rows * 4
+    assert binding.attn_decode_workspace_size(plan, 32, 128) == expect
+    st, plan, _, _ = _plan([100, 100], chunk=0)
+    assert plan.n_partial_slots == 0
+    assert binding.attn_decode_workspace_size(plan, 32, 128) == 0
+
+
+def _host_kv(seqlens, table, num_pages, P=64):
+    import torch
+
+    kv = binding.PagedKV()
+    seqlens = np.ascontiguousarray(seqlens, np.int32)
+    table = np.ascontiguousarray(table, np.int32)
+    kv.page_table, kv.seqlens = table.ctypes.data, seqlens.ctypes.data
+    kv.batch, kv.max_pages_per_seq = table.shape
+    kv.page_size, kv.num_pages = P, num_pages
+    kv.pool0 = 4096
+    return kv, (seqlens, table)
+
+
+def test_paged_kv_check():
+    table = np.array([[0, 3, -1], [2, 1, -1]], np.int32)
+    kv, keep = _host_kv([100, 65], table, 4)
+    assert binding.attn_paged_kv_check(kv) == 0
+    kv, keep = _host_kv([100, 129], table, 4)      # needs a third page: -1
+    assert binding.attn_paged_kv_check(kv) == binding.ATTN_ERR_INVALID_ARG
+    kv, keep = _host_kv([100, 65], table, 3)       # page id 3 out of range
+    assert binding.attn_paged_kv_check(kv) == binding.ATTN_ERR_INVALID_ARG
+    kv, keep = _host_kv([200, 65], table, 4)       # longer than the table allows
+    assert binding.attn_paged_kv_check(kv) == binding.ATTN_ERR_INVALID_ARG
+
+
+def _fake_call(kind="gqa", **over):
+    """A decode call with fake (never dereferenced) aligned device pointers:
+    validation must reject it before any launch."""
+    st, plan, _, _ = _plan([100, 200], groups=over.pop("plan_groups", 8), chunk=64)
+    plan.items, plan.seqinfo = 0x10000, 0x20000
+    kv = binding.PagedKV()
+    kv.pool0, kv.pool1, kv.rope_pool = 0x100000, 0x200000, 0x300000
+    kv.page_table, kv.seqlens = 0x400000, 0x500000
+    kv.batch, kv.max_pages_per_seq, kv.page_size, kv.num_pages = 2, 4, 64, 8
+    kv.page_stride, kv.token_stride, kv.head_stride = 64 * 8 * 128, 8 * 128, 128
+    kv.rope_page_stride, kv.rope_token_stride = 64 * 64, 64
+    kv.dtype = binding.ATTN_BF16
+    args = dict(q=0x600000, out=0x700000, lse=0, q_len=1, h_q=32, groups=8, d=128,
+                ws=0x800000, ws_bytes=0)
+    for k, v in over.items():
+        if hasattr(kv, k):
+            setattr(kv, k, v)
+        else:
+            args[k] = v
+    if kind == "gqa":
+        return binding.attn_decode_gqa(kv, args["q"], args["out"], args["lse"], args["q_len"],
+                                       args["h_q"], args["groups"], args["d"], 0.1, 0, plan,
+                                       args["ws"], args["ws_bytes"], None)
+    if kind == "gta":
+        return binding.attn_decode_gta(kv, args["q"], args["out"], args["lse"], args["q_len"],
+                                       args["h_q"], args["groups"], args["d"],
+                                       args.get("d_rope", 64), args.get("n_rope", 1), 10000.0,
+                                       0.1, 0, plan, args["ws"], args["ws_bytes"], None)
+    return binding.attn_decode_latent(kv, args["q"], args["out"], args["lse"], args["q_len"],
+                                      args["h_q"], args["groups"], args["d"],
+                                      args.get("d_rope", 64), 0.1, 0, plan, args["ws"],
+                                      args["ws_bytes"], None)
+
+
+def test_validation_rejects_before_launch():
+    E, U, WS = binding.ATTN_ERR_INVALID_ARG, binding.ATTN_ERR_UNSUPPORTED, binding.ATTN_ERR_WORKSPACE
+    assert _fake_call(q=0) == E
+    assert _fake_call(pool1=None) == E
+    assert _fake_call(page_size=48) == E                 # not a power of two
+    assert _fake_call(pool0=0x100008) == E               # misaligned pool
+    assert _fake_call(token_stride=8 * 128 + 4) == E     # misaligned rows
+    assert _fake_call(h_q=30) == E                       # h_q % groups
+    assert _fake_call(batch=3) == E                      # plan / descriptor mismatch
+    assert _fake_call(q_len=2) == E                      # plan made for q_len 1
+    assert _fake_call(q_len=17) == E
+    assert _fake_call() == WS                            # splits need workspace
+    assert _fake_call(ws=0x800010, ws_bytes=1 << 30) == WS   # misaligned workspace
+    assert _fake_call(d=96, ws_bytes=1 << 30) == U
+    assert _fake_call("gta", ws_bytes=1 << 30, d_rope=32) == U
+    assert _fake_call("gta", ws_bytes=1 << 30, n_rope=2) == E
+    assert _fake_call("gta", ws_bytes=1 << 30, rope_pool=None) == E
+    assert _fake_call("latent", ws_bytes=1 << 30, d=384, groups=2, plan_groups=2) == U
+    assert _fake_call("latent", ws_bytes=1 << 30, dtype=binding.ATTN_FP32, d=256, groups=2,
+                      plan_groups=2) == U

@@ -1,0 +1,179 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Small cases run the oracle on every output; they span several 64-key tiles
+with ragged tails, forced and automatic splits, every variant and the edge
+cases.  Full-size workloads (the launch configuration the benchmark times)
+are checked on sampled sequences plus properties that hold at any size.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from decode_attention_kv_amd import binding, synth
+from tests import gpu_helpers as H
+
+pytestmark = pytest.mark.gpu
+
+W = synth.WORKLOADS
+
+
+def small(base, **kw):
+    return W[base].with_(**kw)
+
+
+SMALL = {
+    "gqa_fp32_tiny": W["gqa_fp32_tiny"],
+    "gqa_fp32_d128": small("gqa_fp32_tiny", head_dim=128, seqlen_lo=1, seqlen_hi=500,
+                           page_size=16, max_seqlen=512, permute_pages=True, batch=3),
+    "gqa_llama8b": small("gqa_llama8b", batch=4, seqlen_lo=1, seqlen_hi=700, max_seqlen=704),
+    "gqa_d64_mqa": small("gqa_llama8b", batch=3, groups=1, head_dim=64, seqlen_lo=30,
+                         seqlen_hi=300, max_seqlen=320, softmax_scale=0.125),
+    "gqa_mha": small("gqa_llama8b", batch=2, h_q=8, groups=8, seqlen_lo=60, seqlen_hi=260,
+                     max_seqlen=320),
+    "gqa_causal3": small("gqa_llama8b", batch=3, q_len=3, causal=True, seqlen_lo=3,
+                         seqlen_hi=400, max_seqlen=448),
+    "gta_8k": small("gta_8k", batch=3, seqlen_lo=100, seqlen_hi=1000, max_seqlen=1024),
+    "gqa4_8k": small("gqa4_8k", batch=3, seqlen_lo=100, seqlen_hi=1000, max_seqlen=1024),
+    "gta_causal2": small("gta_8k", batch=2, q_len=2, causal=True, seqlen_lo=2,
+                         seqlen_hi=300, max_seqlen=320),
+    "mla": small("mla", batch=2, seqlen_lo=64, seqlen_hi=600, max_seqlen=640),
+    "gla2": small("gla2", batch=2, seqlen_lo=64, seqlen_hi=600, max_seqlen=640),
+    "gla2_spec4": small("gla2_spec4_128k", batch=2, seqlen_lo=4, seqlen_hi=700, max_seqlen=704),
+    "mla_spec4": small("mla_spec4_128k", batch=2, seqlen_lo=4, seqlen_hi=500, max_seqlen=512),
+    "gla2_h32": small("gla2", batch=2, h_q=32, seqlen_lo=1, seqlen_hi=300, max_seqlen=320),
+}
+
+
+def _check(w, inp, tag, **kw):
+    d = H.to_device(w, inp)
+    out, lse, plan = H.run(w, d, **kw)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.decode(w, inp)
+    H.compare(H.to_np(out), H.to_np(lse), ref, ref_lse, H.value_max(w, inp), tag)
+    return out, lse, plan
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+@pytest.mark.parametrize("chunk", [0, 64, 192])
+def test_small_parity(name, chunk):
+    w = SMALL[name]
+    print(f"[parity] {name} chunk={chunk}", flush=True)
+    inp = synth.make_inputs(w)
+    _check(w, inp, f"{name}/chunk{chunk}", chunk_tokens=chunk)
+
+
+@pytest.mark.parametrize("name", ["gqa_llama8b", "gta_8k", "gla2_spec4", "mla"])
+def test_nan_sentinels_in_unused_slots(name):
+    w = SMALL[name]
+    print(f"[nan] {name}", flush=True)
+    inp = synth.make_inputs(w, tail_fill=np.nan, extra_pages=7)
+    _check(w, inp, f"{name}/nan", chunk_tokens=128)
+
+
+@pytest.mark.parametrize("page_size", [1, 16, 256])
+def test_page_sizes(page_size):
+    w = SMALL["gla2"].with_(page_size=page_size, max_seqlen=768)
+    print(f"[page] {page_size}", flush=True)
+    _check(w, synth.make_inputs(w), f"P{page_size}")
+
+
+def test_empty_and_single_token_sequences():
+    w = SMALL["gqa_llama8b"]
+    inp = synth.make_inputs(w, seqlens=np.array([0, 1, 65, 0], dtype=np.int32))
+    out, lse, _ = _check(w, inp, "empty", chunk_tokens=64)
+    o = H.to_np(out)
+    assert (o[0] == 0).all() and (o[3] == 0).all()
+    assert np.isneginf(H.to_np(lse)[[0, 3]]).all()
+
+
+def test_minimum_causal_length():
+    w = SMALL["gla2_spec4"]
+    inp = synth.make_inputs(w, seqlens=np.array([4, 5], dtype=np.int32))
+    _check(w, inp, "causal-min")
+
+
+def test_physical_permutation_is_bit_exact():
+    w = SMALL["gta_8k"]
+    inp = synth.make_inputs(w)
+    out1, lse1, _ = _check(w, inp, "perm-a", chunk_tokens=128)
+    # same logical cache under a different physical page permutation
+    rng = np.random.default_rng(2024)
+    n = inp["pool0"].shape[0]
+    perm = rng.permutation(n)
+    inv = np.argsort(perm)
+    inp2 = dict(inp)
+    inp2["pool0"] = inp["pool0"][perm]
+    inp2["rope"] = inp["rope"][perm]
+    t = inp["page_table"].copy()
+    t[t >= 0] = inv[t[t >= 0]]
+    inp2["page_table"] = t
+    out2, lse2, _ = H.run(w, H.to_device(w, inp2), chunk_tokens=128)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
+
+
+def test_run_to_run_determinism():
+    w = SMALL["mla"]
+    inp = synth.make_inputs(w)
+    d = H.to_device(w, inp)
+    o1, l1, plan = H.run(w, d, chunk_tokens=128)
+    o2, l2, _ = H.run(w, d, plan=plan)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_gather_probe_recovers_physical_rows():
+    """V rows encode their own (page, slot) as exact integers; a query that
+    dominates one chosen key must return exactly that key's code."""
+    w = W["gqa_fp32_tiny"].with_(batch=2, groups=1, h_q=1, head_dim=64, seqlen_lo=200,
+                                 seqlen_hi=200, page_size=16, max_seqlen=256,
+                                 permute_pages=True, softmax_scale=1.0)
+    inp = synth.make_inputs(w)
+    kp = np.zeros_like(inp["pool0"])
+    vp = np.zeros_like(inp["pool1"])
+    npages = kp.shape[0]
+    for pg in range(npages):
+        for sl in range(w.page_size):
+            vp[pg, sl, 0, :] = pg * 1000 + sl
+    targets = [137, 41]
+    q = np.zeros_like(inp["q"])
+    for b, tgt in enumerate(targets):
+        pg = inp["page_table"][b, tgt // w.page_size]
+        kp[pg, tgt % w.page_size, 0, 0] = 1.0
+        q[b, 0, 0, 0] = 200.0
+    inp.update(pool0=kp, pool1=vp, q=q)
+    out, _, _ = H.run(w, H.to_device(w, inp), chunk_tokens=64)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    for b, tgt in enumerate(targets):
+        pg = inp["page_table"][b, tgt // w.page_size]
+        assert np.all(np.rint(o[b, 0, 0]) == pg * 1000 + tgt % w.page_size)
+
+
+# ------------------------------------------------------------ full size
+FULL = ["gqa_fp32_tiny", "gqa_llama8b", "gta_8k", "mla", "gla2", "gla2_spec4_128k"]
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled(name):
+    w = W[name]
+    print(f"[full] {name}", flush=True)
+    inp = synth.make_inputs(w)
+    d = H.to_device(w, inp)
+    out, lse, plan = H.run(w, d)
+    torch.cuda.synchronize()
+    o = H.to_np(out)
+    l = H.to_np(lse)
+    # properties on every row: finite, and each output is a convex
+    # combination of its values, so bounded by the largest |value|
+    assert np.isfinite(o).all() and np.isfinite(l).all()
+    assert np.abs(o).max() <= H.value_max(w, inp) * (1 + 2 ** -7)
+    # sampled sequences against the oracle (longest, shortest, one random)
+    L = inp["seqlens"]
+    pick = sorted({int(np.argmax(L)), int(np.argmin(L)), int(np.random.default_rng(0).integers(len(L)))})
+    ref, ref_lse = oracle.decode(w, inp, batch_index=pick)
+    H.compare(o[pick], l[pick], ref, ref_lse, H.value_max(w, inp, pick), f"{name}/full")
+    del d, out, lse
+    torch.cuda.empty_cache()
