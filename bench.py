@@ -1,0 +1,321 @@
+#!/usr/bin/env python3
+"""Benchmark of paged-KV decode attention on one MI355X.
+
+One step is the whole hot path over one batch: the host split plan, its
+upload, the split-KV decode kernel and the log-sum-exp merge kernel.  Inputs
+are seeded and synthetic and sit in HBM before timing starts.  Before every
+timed step a 1 GiB read evicts the caches (L2 and the 256 MB Infinity
+Cache) outside the timed interval, so every step reads its cache from HBM
+(a read leaves no dirty lines whose write-back would compete with the step).
+
+Prints one JSON line: KV GB/s (algorithmic cache bytes / step time) as the
+value, tokens/s, the decode kernel's roofline (achieved GB/s from HIP events
+on the launch stream vs the 8 TB/s HBM peak) and the fp64 oracle timed on a
+bounded sample on the host cores.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+KERNEL_SRC = os.path.join(ROOT, "decode_attention_kv_amd", "csrc", "attn_decode.hip")
+DESCRIPTIONS = {
+    "gqa_llama8b": "GQA decode, Llama-3-8B layer: bf16, B=32, q_len=1, h_q=32, h_kv=8, d=128, "
+                   "seqlen ~ U[1024,8192], page 64, permuted page table",
+    "gqa_llama8b_8k": "GQA decode, Llama-3-8B layer at 8K: bf16, B=32, h_q=32, h_kv=8, d=128, "
+                      "seqlen 8192, page 64, permuted",
+    "gta_8k": "GTA decode: bf16, B=64, h_q=32, 4 tied heads x 128 + one 64-wide RoPE key "
+              "(theta 1e4, in-kernel), seqlen 8192, page 64, permuted",
+    "gqa4_8k": "GQA-4 at the GTA shape: bf16, B=64, h_q=32, h_kv=4, d=128, seqlen 8192",
+    "mla": "MLA latent decode: bf16, B=128, h_q=128, d_c=512 + RoPE 64, seqlen ~ U[2048,32768]",
+    "gla2": "GLA-2 latent decode: bf16, B=128, h_q=128, 2 x d_c=256 + RoPE 64, "
+            "seqlen ~ U[2048,32768]",
+    "gla2_spec4_128k": "GLA-2 speculative verify: bf16, B=16, q_len=4 causal, h_q=128, "
+                       "2 x 256 + 64, seqlen 131072",
+    "mla_spec4_128k": "MLA speculative verify: bf16, B=16, q_len=4 causal, h_q=128, 512 + 64, "
+                      "seqlen 131072",
+    "gqa_fp32_tiny": "GQA decode fp32 tiny: B=2, h_q=8, h_kv=2, d=64, seqlen 256",
+}
+
+
+def kv_bytes(w, seqlens):
+    """Algorithmic cache bytes of one step: every cached element of every
+    token read once (K and V, or tied state + RoPE key, or latent + RoPE)."""
+    if w.kind == "gqa":
+        per_tok = 2 * w.groups * w.head_dim * w.elem_bytes
+    else:
+        per_tok = (w.groups * w.head_dim + w.d_rope) * w.elem_bytes
+    return int(sum(int(L) for L in seqlens)) * per_tok
+
+
+def flops(w, seqlens):
+    """2 FLOPs per multiply-add of QK^T and P.V over every visible
+    (query row, key) pair."""
+    per = 4 * w.head_dim if w.kind != "latent" else 2 * (w.head_dim + w.d_rope) + 2 * w.head_dim
+    pairs = 0
+    for L in seqlens:
+        L = int(L)
+        pairs += sum(L - w.q_len + 1 + t for t in range(w.q_len)) if (w.causal and w.q_len > 1) \
+            else L * w.q_len
+    return pairs * w.h_q * per
+
+
+def kernel_sha():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(workload, sha):
+    """HBM bytes per decode launch from committed rocprofv3 counter runs,
+    only if they were taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"decode_kernel_{workload}_counters.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != sha:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, inp, seconds):
+    """The fp64 oracle on a bounded sample of the same batch (whole sequences,
+    in batch order, until about `seconds` of work)."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    done, t_used = [], 0.0
+    for b in range(w.batch):
+        t0 = time.perf_counter()
+        oracle.decode(w, inp, batch_index=[b])
+        t_used += time.perf_counter() - t0
+        done.append(b)
+        if t_used >= seconds:
+            break
+    L = inp["seqlens"][done]
+    kvb = oracle.kv_bytes(w, L)
+    return {"value": kvb / t_used / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(done)} of {w.batch} sequences (lengths {int(L.min())}..{int(L.max())}, "
+                      f"{int(L.sum())} tokens) in {t_used:.1f} s; tokens/s "
+                      f"{float(L.sum()) * w.q_len / t_used:.1f}"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gqa_llama8b")
+    ap.add_argument("--flush", choices=["read", "write", "none"], default="read",
+                    help="evict L2 / Infinity Cache before each timed step by reading (default) "
+                         "or writing a 1 GiB buffer, outside the timed interval")
+    ap.add_argument("--layout", choices=["nhd", "hnd"], default="hnd",
+                    help="pool layout: [pages][page][heads][width] (nhd) or "
+                         "[pages][heads][page][width] (hnd), passed to the kernel as strides")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--chunk-tokens", type=int, default=0, help="force the split chunk size")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures the single-GPU decode path only; run it with --gpus 1 "
+              "(sharding across GPUs is described, not built).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from decode_attention_kv_amd import binding, synth
+
+    dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 3}))
+        return
+
+    w = synth.WORKLOADS[args.workload]
+    print(f"[bench] drawing inputs for {w.name}", file=sys.stderr, flush=True)
+    inp = synth.make_inputs(w)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    def dev_t(a):
+        return None if a is None else torch.from_numpy(a).to(dt).to(dev)
+
+    def dev_pool(a):
+        t = dev_t(a)
+        if t is None or args.layout == "nhd":
+            return t
+        # same logical [pages][page][heads][width] view over head-major storage
+        return t.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+
+    q = dev_t(inp["q"])
+    pool0, pool1, rope = dev_pool(inp["pool0"]), dev_pool(inp["pool1"]), dev_pool(inp["rope"])
+    page_table = torch.from_numpy(inp["page_table"]).to(dev)
+    seqlens = torch.from_numpy(inp["seqlens"]).to(dev)
+    seqlens_host = np.ascontiguousarray(inp["seqlens"], dtype=np.int32)
+    B, T, H = w.batch, w.q_len, w.h_q
+    d_v = w.head_dim
+    kv = binding.paged_kv(pool0, pool1, rope, page_table, seqlens)
+    shp = binding.shape(w.kind, kv.dtype, B, T, H, w.groups, w.head_dim, w.d_rope, w.page_size,
+                        w.causal)
+    cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    flags = (binding.ATTN_CAUSAL if w.causal else 0) | binding.ATTN_DEFER_MERGE
+
+    max_items = binding.attn_decode_plan_max_items(B, w.groups, int(max(1, seqlens_host.max())))
+    # two pinned host plan buffers (a step rewrites one while the other may
+    # still be in flight to the device) and one device copy
+    items_h = [torch.zeros((max_items, 4), dtype=torch.int32).pin_memory() for _ in range(2)]
+    info_h = [torch.zeros((B, 4), dtype=torch.int32).pin_memory() for _ in range(2)]
+    copied = [torch.cuda.Event(), torch.cuda.Event()]
+    items_d = torch.zeros((max_items, 4), dtype=torch.int32, device=dev)
+    info_d = torch.zeros((B, 4), dtype=torch.int32, device=dev)
+
+    def make_plan(k):
+        i = k % 2
+        copied[i].synchronize()
+        st, plan = binding.attn_decode_plan(shp, seqlens_host, cu, args.chunk_tokens,
+                                            items_h[i].numpy(), info_h[i].numpy(), max_items)
+        if st != binding.ATTN_OK:
+            raise binding.AttnError(st, "attn_decode_plan")
+        items_d[:plan.n_items].copy_(items_h[i][:plan.n_items], non_blocking=True)
+        info_d.copy_(info_h[i], non_blocking=True)
+        copied[i].record()
+        plan.items, plan.seqinfo = items_d.data_ptr(), info_d.data_ptr()
+        return plan
+
+    plan0 = make_plan(0)
+    torch.cuda.synchronize()
+    ws_bytes = binding.attn_decode_workspace_size(plan0, H, d_v)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, T, H, d_v), dtype=dt, device=dev)
+    lse = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+    flush = None if args.flush == "none" else torch.ones(1 << 28, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    s = stream.cuda_stream
+
+    def step(k, evs=None):
+        if evs is not None:
+            evs[0].record(stream)
+        plan = make_plan(k)
+        if evs is not None:
+            evs[1].record(stream)
+        if w.kind == "gqa":
+            st = binding.attn_decode_gqa(kv, q.data_ptr(), out.data_ptr(), lse.data_ptr(), T, H,
+                                         w.groups, d_v, w.softmax_scale, flags, plan,
+                                         ws.data_ptr(), ws_bytes, s)
+        elif w.kind == "gta":
+            st = binding.attn_decode_gta(kv, q.data_ptr(), out.data_ptr(), lse.data_ptr(), T, H,
+                                         w.groups, d_v, w.d_rope, 1, w.rope_theta,
+                                         w.softmax_scale, flags, plan, ws.data_ptr(), ws_bytes, s)
+        else:
+            st = binding.attn_decode_latent(kv, q.data_ptr(), out.data_ptr(), lse.data_ptr(), T,
+                                            H, w.groups, d_v, w.d_rope, w.softmax_scale, flags,
+                                            plan, ws.data_ptr(), ws_bytes, s)
+        if st != binding.ATTN_OK:
+            raise binding.AttnError(st, "decode")
+        if evs is not None:
+            evs[2].record(stream)
+        st = binding.attn_decode_merge(plan, H, d_v, kv.dtype, ws.data_ptr(), ws_bytes,
+                                       out.data_ptr(), lse.data_ptr(), s)
+        if st != binding.ATTN_OK:
+            raise binding.AttnError(st, "merge")
+        if evs is not None:
+            evs[3].record(stream)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    for k in range(args.steps):
+        if args.flush == "write":
+            flush.fill_(k)
+        elif args.flush == "read":
+            flush.max()
+        step(k, evs[k])
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+
+    step_ms = np.array([e[0].elapsed_time(e[3]) for e in evs])
+    dec_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    merge_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
+    kvb = kv_bytes(w, seqlens_host)
+    fl = flops(w, seqlens_host)
+    ms = float(step_ms.mean())
+    gbps = kvb / (ms * 1e-3) / 1e9
+    dec_gbps = kvb / (float(dec_ms.mean()) * 1e-3) / 1e9
+    dec_tflops = fl / (float(dec_ms.mean()) * 1e-3) / 1e12
+    tokens = B * T
+    sha = kernel_sha()
+
+    # output sanity on the last step (the parity tests do the real check)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all().item(), "non-finite output"
+
+    roofline = {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
+                "traffic": load_traffic(w.name, sha),
+                "algorithmic_bytes_per_launch": int(kvb),
+                "mfma_tflops": round(dec_tflops, 1),
+                "mfma_frac": round(dec_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                "kernel_ms_mean": round(float(dec_ms.mean()), 5),
+                "kernel_source_sha256_16": sha}
+
+    line = {"metric": "decode-attn KV GB/s (% of MI355X HBM peak) and tokens/s at 8K ctx",
+            "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+            "config": {"workload": f"{w.name}: {DESCRIPTIONS.get(w.name, w.name)}",
+                       "batch": B, "q_len": T, "h_q": H, "groups": w.groups,
+                       "head_dim": w.head_dim, "d_rope": w.d_rope,
+                       "mean_seqlen": float(seqlens_host.mean()), "page_size": w.page_size,
+                       "kv_bytes_per_step": int(kvb), "gpus": 1, "layout": args.layout,
+                       "cache_flush": args.flush},
+            "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
+            "tokens_per_s": round(tokens / (ms * 1e-3), 1),
+            "step_ms_median": round(float(np.median(step_ms)), 5),
+            "decode_ms_mean": round(float(dec_ms.mean()), 5),
+            "merge_ms_mean": round(float(merge_ms.mean()), 5),
+            "wall_ms_per_step_incl_flush": round(1e3 * t_wall / args.steps, 5),
+            "plan": {"items": int(plan0.n_items), "max_splits": int(plan0.max_splits),
+                     "partial_slots": int(plan0.n_partial_slots)},
+            "roofline": roofline}
+    if not args.no_cpu_baseline:
+        print("[bench] oracle cpu baseline", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -25,6 +25,9 @@ ATTN_ERR_WORKSPACE = -3
 ATTN_ERR_HIP = -4
 ATTN_FP32 = 0
 ATTN_BF16 = 1
+ATTN_CAUSAL = 1
+ATTN_DEFER_MERGE = 2
+ATTN_KIND = {"gqa": 0, "gta": 1, "latent": 2}
 TILE = 64
 
 
@@ -35,6 +38,18 @@ class PagedKV(Structure):
                 ("page_stride", c_int64), ("token_stride", c_int64), ("head_stride", c_int64),
                 ("rope_page_stride", c_int64), ("rope_token_stride", c_int64),
                 ("rope_head_stride", c_int64), ("dtype", c_int)]
+
+
+class Shape(Structure):
+    _fields_ = [("kind", c_int), ("dtype", c_int), ("batch", c_int32), ("q_len", c_int32),
+                ("h_q", c_int32), ("groups", c_int32), ("head_dim", c_int32), ("d_rope", c_int32),
+                ("page_size", c_int32), ("flags", c_int32)]
+
+
+def shape(kind: str, dtype: int, batch: int, q_len: int, h_q: int, groups: int, head_dim: int,
+          d_rope: int, page_size: int, causal: bool) -> Shape:
+    return Shape(ATTN_KIND[kind], dtype, batch, q_len, h_q, groups, head_dim, d_rope, page_size,
+                 ATTN_CAUSAL if causal else 0)
 
 
 class Plan(Structure):
@@ -64,8 +79,8 @@ def lib():
     L.attn_status_string.restype = c_char_p
     L.attn_decode_plan_max_items.argtypes = [c_int, c_int, c_int]
     L.attn_decode_plan_max_items.restype = c_int
-    L.attn_decode_plan.argtypes = [c_void_p, c_int, c_int, c_int, c_int, c_int, c_int, c_int,
-                                   c_int, c_int, c_void_p, c_void_p, c_int, POINTER(Plan)]
+    L.attn_decode_plan.argtypes = [POINTER(Shape), c_void_p, c_int, c_int, c_void_p, c_void_p,
+                                   c_int, POINTER(Plan)]
     L.attn_decode_plan.restype = c_int
     L.attn_decode_workspace_size.argtypes = [POINTER(Plan), c_int, c_int]
     L.attn_decode_workspace_size.restype = c_size_t
@@ -79,6 +94,9 @@ def lib():
     L.attn_decode_latent.argtypes = ([POINTER(PagedKV), c_void_p, c_void_p, c_void_p, c_int, c_int,
                                       c_int, c_int, c_int] + common_tail)
     L.attn_decode_latent.restype = c_int
+    L.attn_decode_merge.argtypes = [POINTER(Plan), c_int, c_int, c_int, c_void_p, c_size_t,
+                                    c_void_p, c_void_p, c_void_p]
+    L.attn_decode_merge.restype = c_int
     L.attn_paged_kv_check.argtypes = [POINTER(PagedKV)]
     L.attn_paged_kv_check.restype = c_int
     _lib = L
@@ -94,17 +112,15 @@ def attn_decode_plan_max_items(batch: int, n_groups: int, max_seqlen: int) -> in
     return lib().attn_decode_plan_max_items(batch, n_groups, max_seqlen)
 
 
-def attn_decode_plan(seqlens_host: np.ndarray, batch: int, q_len: int, h_q: int, n_groups: int,
-                     token_bytes: int, d_v: int, cu_count: int, chunk_tokens: int, causal: int,
+def attn_decode_plan(shape_: Shape, seqlens_host: np.ndarray, cu_count: int, chunk_tokens: int,
                      items_host: np.ndarray, seqinfo_host: np.ndarray, max_items: int):
     """Returns (status, Plan).  Host numpy arrays, int32, C-contiguous."""
     for a in (seqlens_host, items_host, seqinfo_host):
         assert a.dtype == np.int32 and a.flags.c_contiguous
     plan = Plan()
-    st = lib().attn_decode_plan(seqlens_host.ctypes.data, batch, q_len, h_q, n_groups,
-                                token_bytes, d_v, cu_count, chunk_tokens, int(causal),
-                                items_host.ctypes.data, seqinfo_host.ctypes.data, max_items,
-                                ctypes.byref(plan))
+    st = lib().attn_decode_plan(ctypes.byref(shape_), seqlens_host.ctypes.data, cu_count,
+                                chunk_tokens, items_host.ctypes.data, seqinfo_host.ctypes.data,
+                                max_items, ctypes.byref(plan))
     return st, plan
 
 
@@ -112,23 +128,28 @@ def attn_decode_workspace_size(plan: Plan, h_q: int, d_v: int) -> int:
     return lib().attn_decode_workspace_size(ctypes.byref(plan), h_q, d_v)
 
 
-def attn_decode_gqa(kv, q, out, lse, q_len, h_q, h_kv, d, scale, causal, plan, ws, ws_bytes,
+def attn_decode_gqa(kv, q, out, lse, q_len, h_q, h_kv, d, scale, flags, plan, ws, ws_bytes,
                     stream) -> int:
     return lib().attn_decode_gqa(ctypes.byref(kv), q, out, lse, q_len, h_q, h_kv, d, scale,
-                                 causal, ctypes.byref(plan), ws, ws_bytes, stream)
+                                 flags, ctypes.byref(plan), ws, ws_bytes, stream)
 
 
 def attn_decode_gta(kv, q, out, lse, q_len, h_q, h_kv, d, d_rope, n_rope_heads, rope_theta,
-                    scale, causal, plan, ws, ws_bytes, stream) -> int:
+                    scale, flags, plan, ws, ws_bytes, stream) -> int:
     return lib().attn_decode_gta(ctypes.byref(kv), q, out, lse, q_len, h_q, h_kv, d, d_rope,
-                                 n_rope_heads, rope_theta, scale, causal, ctypes.byref(plan), ws,
+                                 n_rope_heads, rope_theta, scale, flags, ctypes.byref(plan), ws,
                                  ws_bytes, stream)
 
 
-def attn_decode_latent(kv, q, out, lse, q_len, h_q, h_c, d_c, d_rope, scale, causal, plan, ws,
+def attn_decode_latent(kv, q, out, lse, q_len, h_q, h_c, d_c, d_rope, scale, flags, plan, ws,
                        ws_bytes, stream) -> int:
     return lib().attn_decode_latent(ctypes.byref(kv), q, out, lse, q_len, h_q, h_c, d_c, d_rope,
-                                    scale, causal, ctypes.byref(plan), ws, ws_bytes, stream)
+                                    scale, flags, ctypes.byref(plan), ws, ws_bytes, stream)
+
+
+def attn_decode_merge(plan, h_q, d_v, dtype, ws, ws_bytes, out, lse, stream) -> int:
+    return lib().attn_decode_merge(ctypes.byref(plan), h_q, d_v, dtype, ws, ws_bytes, out, lse,
+                                   stream)
 
 
 def attn_paged_kv_check(kv: PagedKV) -> int:
@@ -171,20 +192,19 @@ def paged_kv(pool0, pool1, rope, page_table, seqlens) -> PagedKV:
 class DevicePlan:
     """A host plan plus its device copy (keeps the device arrays alive)."""
 
-    def __init__(self, seqlens_host, q_len, h_q, n_groups, token_bytes, d_v, device,
-                 cu_count=256, chunk_tokens=0, causal=False):
+    def __init__(self, shape_: Shape, seqlens_host, device, cu_count=256, chunk_tokens=0):
         import torch
 
         seqlens_host = np.ascontiguousarray(seqlens_host, dtype=np.int32)
         batch = len(seqlens_host)
-        max_items = attn_decode_plan_max_items(batch, n_groups, int(max(1, seqlens_host.max(initial=0))))
+        max_items = attn_decode_plan_max_items(batch, shape_.groups,
+                                               int(max(1, seqlens_host.max(initial=0))))
         if max_items < 0:
             raise AttnError(max_items, "attn_decode_plan_max_items")
         self.items_host = np.zeros((max_items, 4), dtype=np.int32)
         self.seqinfo_host = np.zeros((batch, 4), dtype=np.int32)
-        st, plan = attn_decode_plan(seqlens_host, batch, q_len, h_q, n_groups, token_bytes, d_v,
-                                    cu_count, chunk_tokens, int(causal), self.items_host,
-                                    self.seqinfo_host, max_items)
+        st, plan = attn_decode_plan(shape_, seqlens_host, cu_count, chunk_tokens,
+                                    self.items_host, self.seqinfo_host, max_items)
         if st != ATTN_OK:
             raise AttnError(st, "attn_decode_plan")
         self.items_dev = torch.from_numpy(self.items_host[:plan.n_items].copy()).to(device)
@@ -194,30 +214,26 @@ class DevicePlan:
         self.plan = plan
 
 
-def token_bytes(kind: str, head_dim: int, d_rope: int, elem: int) -> int:
-    if kind == "gqa":
-        return 2 * head_dim * elem
-    return (head_dim + d_rope) * elem
-
-
 def decode(kind: str, q, pool0, pool1, rope, page_table, seqlens, seqlens_host, *, groups: int,
            scale: float, causal: bool = False, rope_theta: float = 0.0, d_rope: int = 0,
            out=None, lse=None, chunk_tokens: int = 0, cu_count: int = 256, plan=None,
-           workspace=None, stream=None):
+           workspace=None, stream=None, defer_merge: bool = False):
     """Run one decode through the native library on torch tensors.
 
     kind: "gqa" | "gta" | "latent".  q [B, T, H, Dq]; pools as in the header.
     Returns (out, lse, plan, workspace) so callers can reuse plan/workspace.
+    With ``defer_merge`` the split partials stay in the workspace and the
+    caller finishes with ``merge``.
     """
     import torch
 
     B, T, H, _ = q.shape
     width = pool0.shape[-1]
     d_v = width
-    elem = pool0.element_size()
     if plan is None:
-        plan = DevicePlan(seqlens_host, T, H, groups, token_bytes(kind, width, d_rope, elem), d_v,
-                          q.device, cu_count=cu_count, chunk_tokens=chunk_tokens, causal=causal)
+        dtype = ATTN_BF16 if pool0.dtype == torch.bfloat16 else ATTN_FP32
+        sh = shape(kind, dtype, B, T, H, groups, width, d_rope, pool0.shape[1], causal)
+        plan = DevicePlan(sh, seqlens_host, q.device, cu_count=cu_count, chunk_tokens=chunk_tokens)
     need = attn_decode_workspace_size(plan.plan, H, d_v)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
@@ -227,19 +243,34 @@ def decode(kind: str, q, pool0, pool1, rope, page_table, seqlens, seqlens_host, 
         lse = torch.empty((B, T, H), dtype=torch.float32, device=q.device)
     kv = paged_kv(pool0, pool1, rope, page_table, seqlens)
     s = (stream if stream is not None else torch.cuda.current_stream(q.device)).cuda_stream
+    flags = (ATTN_CAUSAL if causal else 0) | (ATTN_DEFER_MERGE if defer_merge else 0)
     if kind == "gqa":
         st = attn_decode_gqa(kv, q.data_ptr(), out.data_ptr(), lse.data_ptr(), T, H, groups, width,
-                             scale, int(causal), plan.plan, workspace.data_ptr(), need, s)
+                             scale, flags, plan.plan, workspace.data_ptr(), need, s)
     elif kind == "gta":
         st = attn_decode_gta(kv, q.data_ptr(), out.data_ptr(), lse.data_ptr(), T, H, groups, width,
-                             d_rope, 1, rope_theta, scale, int(causal), plan.plan,
+                             d_rope, 1, rope_theta, scale, flags, plan.plan,
                              workspace.data_ptr(), need, s)
     elif kind == "latent":
         st = attn_decode_latent(kv, q.data_ptr(), out.data_ptr(), lse.data_ptr(), T, H, groups,
-                                width, d_rope, scale, int(causal), plan.plan,
+                                width, d_rope, scale, flags, plan.plan,
                                 workspace.data_ptr(), need, s)
     else:
         raise ValueError(kind)
     if st != ATTN_OK:
         raise AttnError(st, f"attn_decode_{kind}")
     return out, lse, plan, workspace
+
+
+def merge(plan: DevicePlan, out, lse, workspace, stream=None):
+    """Finish a decode made with ``defer_merge`` (attn_decode_merge)."""
+    import torch
+
+    B, T, H, d_v = out.shape
+    dtype = ATTN_BF16 if out.dtype == torch.bfloat16 else ATTN_FP32
+    need = attn_decode_workspace_size(plan.plan, H, d_v)
+    s = (stream if stream is not None else torch.cuda.current_stream(out.device)).cuda_stream
+    st = attn_decode_merge(plan.plan, H, d_v, dtype, workspace.data_ptr(), need, out.data_ptr(),
+                           None if lse is None else lse.data_ptr(), s)
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_decode_merge")

@@ -2,6 +2,7 @@
 // descriptor checks and status strings.  Integer work only; no GPU calls,
 // so these entry points also run on machines without a GPU.
 #include "attn_decode.h"
+#include "attn_kernels.h"
 
 #include <algorithm>
 #include <cstdint>
@@ -10,16 +11,17 @@
 
 namespace {
 
-constexpr int kTile = 64;  // keys per kernel tile; chunks are multiples of it
+using attn_internal::kTile;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Estimated cost, in bytes-equivalent, of the whole decode for chunks of
 // `ct` tiles: the larger of (total traffic spread over all CUs) and (the
-// longest single work item), which bounds a greedy schedule's makespan.
+// longest single work item, which streams at only 1/W of a CU's bandwidth
+// when W workgroups share the CU), which bounds a greedy schedule's makespan.
 struct CostModel {
   const std::vector<int64_t>* tiles;
-  int64_t groups, token_bytes, split_bytes, item_bytes, cu;
+  int64_t groups, token_bytes, split_bytes, item_bytes, cu, wgs_per_cu;
   double eval(int64_t ct) const {
     int64_t total = 0, longest = 0;
     bool any_split = false;
@@ -34,7 +36,7 @@ struct CostModel {
     // the merge kernel is a second launch: about 2 microseconds of the
     // whole GPU, i.e. what one CU streams in that time
     const double merge = any_split ? 64.0 * 1024.0 : 0.0;
-    return std::max((double)total / (double)cu, (double)longest) + merge;
+    return std::max((double)total / (double)cu, (double)longest * (double)wgs_per_cu) + merge;
   }
 };
 
@@ -61,16 +63,24 @@ int attn_decode_plan_max_items(int batch, int n_groups, int max_seqlen) {
   return (int)n;
 }
 
-int attn_decode_plan(const int32_t* seqlens_host, int batch, int q_len, int h_q,
-                     int n_groups, int token_bytes, int d_v, int cu_count,
-                     int chunk_tokens, int causal, int32_t* items_host,
-                     int32_t* seqinfo_host, int max_items, attn_plan_t* plan) {
-  if (!seqlens_host || !items_host || !seqinfo_host || !plan) return ATTN_ERR_INVALID_ARG;
-  if (batch <= 0 || q_len <= 0 || h_q <= 0 || n_groups <= 0 || token_bytes <= 0 ||
-      d_v <= 0 || cu_count <= 0 || max_items <= 0)
+int attn_decode_plan(const attn_shape_t* shape, const int32_t* seqlens_host, int cu_count,
+                     int chunk_tokens, int32_t* items_host, int32_t* seqinfo_host,
+                     int max_items, attn_plan_t* plan) {
+  if (!shape || !seqlens_host || !items_host || !seqinfo_host || !plan) return ATTN_ERR_INVALID_ARG;
+  const int batch = shape->batch, q_len = shape->q_len, h_q = shape->h_q;
+  const int n_groups = shape->groups;
+  const int causal = shape->flags & ATTN_CAUSAL;
+  if (batch <= 0 || q_len <= 0 || h_q <= 0 || n_groups <= 0 || shape->head_dim <= 0 ||
+      shape->d_rope < 0 || shape->page_size <= 0 || cu_count <= 0 || max_items <= 0)
+    return ATTN_ERR_INVALID_ARG;
+  if (shape->kind != ATTN_KIND_GQA && shape->kind != ATTN_KIND_GTA &&
+      shape->kind != ATTN_KIND_LATENT)
     return ATTN_ERR_INVALID_ARG;
   if (h_q % n_groups) return ATTN_ERR_INVALID_ARG;
   if (chunk_tokens < 0 || chunk_tokens % kTile) return ATTN_ERR_INVALID_ARG;
+  const attn_internal::KernelChoice kc = attn_internal::choose_kernel(*shape);
+  const int64_t token_bytes = kc.token_bytes;
+  const int d_v = kc.d_v;
 
   std::vector<int64_t> tiles(batch);
   int64_t max_tiles = 1;
@@ -97,6 +107,7 @@ int attn_decode_plan(const int32_t* seqlens_host, int batch, int q_len, int h_q,
     // taken as the bytes one CU streams in about 1.5 microseconds
     m.item_bytes = rows * (d_v + 64) * 2 + 48 * 1024;
     m.cu = cu_count;
+    m.wgs_per_cu = kc.wgs_per_cu;
     ct = max_tiles;
     double best = m.eval(ct);
     // candidate chunk lengths: every tile count that changes some split count

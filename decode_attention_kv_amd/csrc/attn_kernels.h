@@ -1,0 +1,67 @@
+// Internal: which decode kernel runs for a problem shape, and the facts the
+// host planner needs about it.  Shared by the planner (attn_host.cpp) and the
+// launchers (attn_decode.hip) so both always agree.
+#ifndef ATTN_KERNELS_H
+#define ATTN_KERNELS_H
+
+#include <cstdint>
+#include <cstdlib>
+
+#include "attn_decode.h"
+
+namespace attn_internal {
+
+constexpr int kTile = 64;          // keys per tile; chunks are multiples of it
+constexpr int kNarrowWaves = 4;    // waves per workgroup of the streaming kernel
+constexpr int kNarrowStageTarget = 65536;  // LDS bytes of the streaming ring
+
+struct KernelChoice {
+  bool narrow;         // streaming kernel (GQA/GTA) vs general kernel
+  int wgs_per_cu;      // workgroups one CU keeps resident
+  int stages;          // streaming ring depth (narrow only)
+  int64_t token_bytes; // cache bytes one work item reads per token
+  int rows;            // query rows per group: (h_q / groups) * q_len
+  int d_v;             // output width per head
+};
+
+// Bytes of one 64-key stage of the streaming kernel (four waves x 16 keys).
+inline int narrow_stage_bytes(int kind, int head_dim, int d_rope) {
+  const int per_key = (kind == ATTN_KIND_GQA) ? 2 * head_dim * 2 : (head_dim + d_rope) * 2;
+  return kNarrowWaves * 16 * per_key;
+}
+
+inline int narrow_stages(int kind, int head_dim, int d_rope) {
+  int s = kNarrowStageTarget / narrow_stage_bytes(kind, head_dim, d_rope);
+  if (const char* e = std::getenv("ATTN_NARROW_STAGES")) s = std::atoi(e);
+  return s < 2 ? 2 : s > 6 ? 6 : s;
+}
+
+inline KernelChoice choose_kernel(const attn_shape_t& sh) {
+  KernelChoice k{};
+  k.rows = (sh.groups > 0 ? sh.h_q / sh.groups : 0) * sh.q_len;
+  k.d_v = sh.head_dim;
+  const int elem = sh.dtype == ATTN_BF16 ? 2 : 4;
+  k.token_bytes = (sh.kind == ATTN_KIND_GQA) ? 2LL * sh.head_dim * elem
+                                             : (int64_t)(sh.head_dim + sh.d_rope) * elem;
+  bool narrow = sh.dtype == ATTN_BF16 && k.rows <= 64 && sh.page_size >= kTile &&
+                ((sh.kind == ATTN_KIND_GQA && (sh.head_dim == 64 || sh.head_dim == 128)) ||
+                 (sh.kind == ATTN_KIND_GTA && sh.head_dim == 128 && sh.d_rope == 64));
+  if (const char* e = std::getenv("ATTN_FORCE_GENERAL")) {
+    if (std::atoi(e)) narrow = false;
+  }
+  k.narrow = narrow;
+  if (narrow) {
+    k.stages = narrow_stages(sh.kind, sh.head_dim, sh.d_rope);
+    const int lds = k.stages * narrow_stage_bytes(sh.kind, sh.head_dim, sh.d_rope) + 2048;
+    int w = 163840 / lds;
+    k.wgs_per_cu = w < 1 ? 1 : w > 2 ? 2 : w;
+  } else {
+    k.stages = 1;
+    k.wgs_per_cu = 1;
+  }
+  return k;
+}
+
+}  // namespace attn_internal
+
+#endif  // ATTN_KERNELS_H

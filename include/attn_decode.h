@@ -64,6 +64,15 @@ typedef enum {
 
 typedef enum { ATTN_FP32 = 0, ATTN_BF16 = 1 } attn_dtype_t;
 
+typedef enum { ATTN_KIND_GQA = 0, ATTN_KIND_GTA = 1, ATTN_KIND_LATENT = 2 } attn_kind_t;
+
+/* Bits of the `flags` argument of the decode calls. */
+enum {
+  ATTN_CAUSAL = 1,      /* q_len > 1: row t sees keys i <= L - q_len + t           */
+  ATTN_DEFER_MERGE = 2  /* leave split partials in the workspace; the caller runs
+                           attn_decode_merge (same stream) to finish the output    */
+};
+
 /*
  * Paged KV cache descriptor ("Hardware-Efficient Attention for Fast
  * Decoding", "If this is right": paged KV with a per-sequence page table).
@@ -125,32 +134,40 @@ typedef struct {
   const int32_t* seqinfo;  /* DEVICE copy of seqinfo_host                        */
 } attn_plan_t;
 
+/*
+ * Shape of a decode call, as the planner needs it.
+ *   kind      GQA, GTA or latent (MLA / GLA)
+ *   groups    KV heads h_kv (GQA/GTA) or latent heads h_c (latent)
+ *   head_dim  d (GQA/GTA) or d_c (latent); d_rope: 0 for GQA
+ *   flags     ATTN_CAUSAL if the call is causal (q_len > 1)
+ */
+typedef struct {
+  attn_kind_t kind;
+  attn_dtype_t dtype;
+  int32_t batch, q_len, h_q, groups, head_dim, d_rope, page_size, flags;
+} attn_shape_t;
+
 /* Upper bound on the work items attn_decode_plan can emit (host-only). */
 int attn_decode_plan_max_items(int batch, int n_groups, int max_seqlen);
 
 /*
  * Build a split plan on the host (integer work only, no GPU calls).
+ *   shape         the decode call's shape (see attn_shape_t)
  *   seqlens_host  host int32 [batch]
- *   q_len, h_q    query tokens per sequence and query heads
- *   n_groups      KV heads (GQA/GTA) or latent heads h_c (latent)
- *   token_bytes   cache bytes one group's work item reads per token
- *                 (GQA 2*d*elem, GTA (d+d_rope)*2, latent (d_c+d_rope)*2)
- *   d_v           output width per head (sizes the split partials)
  *   cu_count      compute units of the target GPU (256 on MI355X)
- *   chunk_tokens  0: automatic split (balances the longest chunk against
+ *   chunk_tokens  0: automatic split (balances the longest chunk, given how
+ *                 many workgroups the chosen kernel keeps per CU, against
  *                 the partial-result traffic that more splits cost);
  *                 > 0: force chunks of this many tokens (multiple of 64)
- *   causal        nonzero: every seqlen must be >= q_len
  *   items_host    host int32 [max_items][4], seqinfo_host host int32 [batch][4]
  * Errors: INVALID_ARG for null pointers, non-positive sizes, negative
  * lengths, causal lengths below q_len, chunk_tokens not a multiple of 64;
  * WORKSPACE if max_items is too small.  On success plan->items and
  * plan->seqinfo are NULL; the caller sets them to the device copies.
  */
-int attn_decode_plan(const int32_t* seqlens_host, int batch, int q_len, int h_q,
-                     int n_groups, int token_bytes, int d_v, int cu_count,
-                     int chunk_tokens, int causal, int32_t* items_host,
-                     int32_t* seqinfo_host, int max_items, attn_plan_t* plan);
+int attn_decode_plan(const attn_shape_t* shape, const int32_t* seqlens_host, int cu_count,
+                     int chunk_tokens, int32_t* items_host, int32_t* seqinfo_host,
+                     int max_items, attn_plan_t* plan);
 
 /*
  * Bytes of device workspace a decode call needs for split partials:
@@ -164,10 +181,14 @@ size_t attn_decode_workspace_size(const attn_plan_t* plan, int h_q, int d_v);
  *   q    [batch][q_len][h_q][d]       dtype of kv->dtype, contiguous
  *   out  [batch][q_len][h_q][d]       same dtype, contiguous
  *   lse  [batch][q_len][h_q] fp32, or NULL
+ *   flags ATTN_CAUSAL and/or ATTN_DEFER_MERGE
+ *   plan, workspace  from attn_decode_plan / attn_decode_workspace_size;
+ *        the workspace must be 256-byte aligned (may be NULL if the plan
+ *        splits nothing)
  * Supported: d in {64, 128}; h_q % h_kv == 0; q_len in [1, 16].
  */
 int attn_decode_gqa(const attn_paged_kv_t* kv, const void* q, void* out, float* lse,
-                    int q_len, int h_q, int h_kv, int d, float softmax_scale, int causal,
+                    int q_len, int h_q, int h_kv, int d, float softmax_scale, int flags,
                     const attn_plan_t* plan, void* workspace, size_t workspace_bytes,
                     hipStream_t stream);
 
@@ -181,7 +202,7 @@ int attn_decode_gqa(const attn_paged_kv_t* kv, const void* q, void* out, float* 
  */
 int attn_decode_gta(const attn_paged_kv_t* kv, const void* q, void* out, float* lse,
                     int q_len, int h_q, int h_kv, int d, int d_rope, int n_rope_heads,
-                    float rope_theta, float softmax_scale, int causal,
+                    float rope_theta, float softmax_scale, int flags,
                     const attn_plan_t* plan, void* workspace, size_t workspace_bytes,
                     hipStream_t stream);
 
@@ -193,8 +214,24 @@ int attn_decode_gta(const attn_paged_kv_t* kv, const void* q, void* out, float* 
  */
 int attn_decode_latent(const attn_paged_kv_t* kv, const void* q, void* out, float* lse,
                        int q_len, int h_q, int h_c, int d_c, int d_rope,
-                       float softmax_scale, int causal, const attn_plan_t* plan,
+                       float softmax_scale, int flags, const attn_plan_t* plan,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Log-sum-exp merge of split partials (the second half of a decode call made
+ * with ATTN_DEFER_MERGE; Hydragen's softmax-denominator decomposition on the
+ * "Efficient Inference" tag page).  For every sequence with n_splits > 1 and
+ * every row: M = max_s lse_s, w_s = exp(lse_s - M),
+ * out = sum_s w_s O_s / sum_s w_s, lse = M + ln sum_s w_s.  Rows of
+ * sequences with one split were already written by the decode call.
+ *   workspace  the decode call's workspace (partials), device
+ *   out        [batch][q_len][h_q][d_v] in `dtype`; lse [batch][q_len][h_q]
+ *              fp32 or NULL
+ * Supported: d_v in {64, 128, 256, 512}.
+ */
+int attn_decode_merge(const attn_plan_t* plan, int h_q, int d_v, attn_dtype_t dtype,
+                      const void* workspace, size_t workspace_bytes, void* out, float* lse,
+                      hipStream_t stream);
 
 /*
  * Host-side consistency check of a descriptor whose page_table and seqlens

@@ -36,13 +36,14 @@ def test_status_strings():
     assert binding.attn_status_string(12345) == "unknown status"
 
 
-def _plan(seqlens, q_len=1, h_q=32, groups=8, tb=512, d_v=128, cu=256, chunk=0, causal=0):
+def _plan(seqlens, q_len=1, h_q=32, groups=8, kind="gqa", d=128, d_rope=0, page=64, cu=256,
+          chunk=0, causal=0, dtype=binding.ATTN_BF16):
     seqlens = np.asarray(seqlens, dtype=np.int32)
     mi = binding.attn_decode_plan_max_items(len(seqlens), groups, int(max(1, seqlens.max())))
     items = np.zeros((mi, 4), np.int32)
     info = np.zeros((len(seqlens), 4), np.int32)
-    st, plan = binding.attn_decode_plan(seqlens, len(seqlens), q_len, h_q, groups, tb, d_v, cu,
-                                        chunk, causal, items, info, mi)
+    sh = binding.shape(kind, dtype, len(seqlens), q_len, h_q, groups, d, d_rope, page, causal)
+    st, plan = binding.attn_decode_plan(sh, seqlens, cu, chunk, items, info, mi)
     return st, plan, items[:max(plan.n_items, 0)], info
 
 
@@ -93,7 +94,8 @@ def test_plan_is_deterministic_and_longest_first():
 def test_plan_auto_split_balances_load():
     # one long sequence must be split so its chunks do not dominate
     seqlens = np.array([131072] * 16, np.int32)
-    st, plan, items, info = _plan(seqlens, q_len=4, h_q=128, groups=2, tb=640, d_v=256)
+    st, plan, items, info = _plan(seqlens, q_len=4, h_q=128, groups=2, kind="latent", d=256,
+                                  d_rope=64, causal=1)
     assert st == 0 and plan.max_splits > 1
     # partial traffic stays a small fraction of the cache bytes
     part = plan.n_partial_slots * 4 * 128 * (256 + 1) * 4 * 2
@@ -109,11 +111,17 @@ def test_plan_errors():
     assert _plan([10, -1])[0] == binding.ATTN_ERR_INVALID_ARG
     assert _plan([2, 20], q_len=4, causal=1)[0] == binding.ATTN_ERR_INVALID_ARG
     assert _plan([10, 20], h_q=30, groups=8)[0] == binding.ATTN_ERR_INVALID_ARG
+    assert _plan([10, 20], kind="gqa", d=0)[0] == binding.ATTN_ERR_INVALID_ARG
     seq = np.array([5000], np.int32)
     items = np.zeros((2, 4), np.int32)
     info = np.zeros((1, 4), np.int32)
-    st, _ = binding.attn_decode_plan(seq, 1, 1, 32, 8, 512, 128, 256, 64, 0, items, info, 2)
+    sh = binding.shape("gqa", binding.ATTN_BF16, 1, 1, 32, 8, 128, 0, 64, False)
+    st, _ = binding.attn_decode_plan(sh, seq, 256, 64, items, info, 2)
     assert st == binding.ATTN_ERR_WORKSPACE
+    bad = binding.shape("gqa", binding.ATTN_BF16, 1, 1, 32, 8, 128, 0, 64, False)
+    bad.kind = 7
+    st, _ = binding.attn_decode_plan(bad, seq, 256, 0, np.zeros((200, 4), np.int32), info, 200)
+    assert st == binding.ATTN_ERR_INVALID_ARG
 
 
 def test_workspace_size():
@@ -165,7 +173,7 @@ def _fake_call(kind="gqa", **over):
     kv.rope_page_stride, kv.rope_token_stride = 64 * 64, 64
     kv.dtype = binding.ATTN_BF16
     args = dict(q=0x600000, out=0x700000, lse=0, q_len=1, h_q=32, groups=8, d=128,
-                ws=0x800000, ws_bytes=0)
+                ws=0x800000, ws_bytes=0, flags=0)
     for k, v in over.items():
         if hasattr(kv, k):
             setattr(kv, k, v)
@@ -173,16 +181,16 @@ def _fake_call(kind="gqa", **over):
             args[k] = v
     if kind == "gqa":
         return binding.attn_decode_gqa(kv, args["q"], args["out"], args["lse"], args["q_len"],
-                                       args["h_q"], args["groups"], args["d"], 0.1, 0, plan,
+                                       args["h_q"], args["groups"], args["d"], 0.1, args["flags"], plan,
                                        args["ws"], args["ws_bytes"], None)
     if kind == "gta":
         return binding.attn_decode_gta(kv, args["q"], args["out"], args["lse"], args["q_len"],
                                        args["h_q"], args["groups"], args["d"],
                                        args.get("d_rope", 64), args.get("n_rope", 1), 10000.0,
-                                       0.1, 0, plan, args["ws"], args["ws_bytes"], None)
+                                       0.1, args["flags"], plan, args["ws"], args["ws_bytes"], None)
     return binding.attn_decode_latent(kv, args["q"], args["out"], args["lse"], args["q_len"],
                                       args["h_q"], args["groups"], args["d"],
-                                      args.get("d_rope", 64), 0.1, 0, plan, args["ws"],
+                                      args.get("d_rope", 64), 0.1, args["flags"], plan, args["ws"],
                                       args["ws_bytes"], None)
 
 
@@ -197,6 +205,7 @@ def test_validation_rejects_before_launch():
     assert _fake_call(batch=3) == E                      # plan / descriptor mismatch
     assert _fake_call(q_len=2) == E                      # plan made for q_len 1
     assert _fake_call(q_len=17) == E
+    assert _fake_call(flags=4, ws_bytes=1 << 30) == E    # unknown flag bit
     assert _fake_call() == WS                            # splits need workspace
     assert _fake_call(ws=0x800010, ws_bytes=1 << 30) == WS   # misaligned workspace
     assert _fake_call(d=96, ws_bytes=1 << 30) == U
@@ -206,3 +215,18 @@ def test_validation_rejects_before_launch():
     assert _fake_call("latent", ws_bytes=1 << 30, d=384, groups=2, plan_groups=2) == U
     assert _fake_call("latent", ws_bytes=1 << 30, dtype=binding.ATTN_FP32, d=256, groups=2,
                       plan_groups=2) == U
+
+
+def test_merge_validation():
+    st, plan, _, _ = _plan([5000, 100], chunk=64)
+    plan.items, plan.seqinfo = 0x10000, 0x20000
+    need = binding.attn_decode_workspace_size(plan, 32, 128)
+    M = binding.attn_decode_merge
+    assert M(plan, 32, 96, binding.ATTN_BF16, 0x800000, need, 0x700000, None, None) == binding.ATTN_ERR_UNSUPPORTED
+    assert M(plan, 32, 128, binding.ATTN_BF16, 0x800000, need - 1, 0x700000, None, None) == binding.ATTN_ERR_WORKSPACE
+    assert M(plan, 32, 128, 7, 0x800000, need, 0x700000, None, None) == binding.ATTN_ERR_INVALID_ARG
+    assert M(plan, 32, 128, binding.ATTN_BF16, 0x800000, need, 0, None, None) == binding.ATTN_ERR_INVALID_ARG
+    st, plan, _, _ = _plan([100, 100])
+    plan.items, plan.seqinfo = 0x10000, 0x20000
+    # nothing split: a no-op that succeeds without touching the GPU
+    assert M(plan, 32, 128, binding.ATTN_BF16, 0, 0, 0x700000, None, None) == binding.ATTN_OK

@@ -123,6 +123,21 @@ def test_run_to_run_determinism():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+@pytest.mark.parametrize("name", ["gqa_llama8b", "gla2_spec4"])
+def test_deferred_merge_matches_fused_call(name):
+    w = SMALL[name]
+    inp = synth.make_inputs(w)
+    d = H.to_device(w, inp)
+    o1, l1, plan = H.run(w, d, chunk_tokens=64)
+    o2, l2, plan2, ws = binding.decode(
+        w.kind, d["q"], d["pool0"], d["pool1"], d["rope"], d["page_table"], d["seqlens"],
+        d["seqlens_host"], groups=w.groups, scale=w.softmax_scale, causal=w.causal,
+        rope_theta=w.rope_theta, d_rope=w.d_rope, plan=plan, defer_merge=True)
+    binding.merge(plan, o2, l2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
 def test_gather_probe_recovers_physical_rows():
     """V rows encode their own (page, slot) as exact integers; a query that
     dominates one chosen key must return exactly that key's code."""
