@@ -26,7 +26,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
-KERNEL_SRC = os.path.join(ROOT, "decode_attention_kv_amd", "csrc", "attn_decode.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "decode_attention_kv_amd", "csrc", f)
+               for f in ("attn_decode.hip", "attn_kernels.h")]
 DESCRIPTIONS = {
     "gqa_llama8b": "GQA decode, Llama-3-8B layer: bf16, B=32, q_len=1, h_q=32, h_kv=8, d=128, "
                    "seqlen ~ U[1024,8192], page 64, permuted page table",
@@ -69,8 +70,13 @@ def flops(w, seqlens):
 
 
 def kernel_sha():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the kernel sources: counter-based traffic is reported only
+    while it was taken on exactly these sources."""
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic(workload, sha):
@@ -190,24 +196,25 @@ def main():
 
     max_items = binding.attn_decode_plan_max_items(B, w.groups, int(max(1, seqlens_host.max())))
     # two pinned host plan buffers (a step rewrites one while the other may
-    # still be in flight to the device) and one device copy
-    items_h = [torch.zeros((max_items, 4), dtype=torch.int32).pin_memory() for _ in range(2)]
-    info_h = [torch.zeros((B, 4), dtype=torch.int32).pin_memory() for _ in range(2)]
+    # still be in flight to the device), each [seqinfo rows | item rows], so a
+    # step uploads its plan with one copy
+    host_buf = [torch.zeros((B + max_items, 4), dtype=torch.int32).pin_memory() for _ in range(2)]
     copied = [torch.cuda.Event(), torch.cuda.Event()]
-    items_d = torch.zeros((max_items, 4), dtype=torch.int32, device=dev)
-    info_d = torch.zeros((B, 4), dtype=torch.int32, device=dev)
+    dev_buf = torch.zeros((B + max_items, 4), dtype=torch.int32, device=dev)
 
     def make_plan(k):
         i = k % 2
         copied[i].synchronize()
-        st, plan = binding.attn_decode_plan(shp, seqlens_host, cu, args.chunk_tokens,
-                                            items_h[i].numpy(), info_h[i].numpy(), max_items)
+        hb = host_buf[i].numpy()
+        st, plan = binding.attn_decode_plan(shp, seqlens_host, cu, args.chunk_tokens, hb[B:],
+                                            hb[:B], max_items)
         if st != binding.ATTN_OK:
             raise binding.AttnError(st, "attn_decode_plan")
-        items_d[:plan.n_items].copy_(items_h[i][:plan.n_items], non_blocking=True)
-        info_d.copy_(info_h[i], non_blocking=True)
+        n = B + plan.n_items
+        dev_buf[:n].copy_(host_buf[i][:n], non_blocking=True)
         copied[i].record()
-        plan.items, plan.seqinfo = items_d.data_ptr(), info_d.data_ptr()
+        plan.seqinfo = dev_buf.data_ptr()
+        plan.items = dev_buf.data_ptr() + B * 16
         return plan
 
     plan0 = make_plan(0)

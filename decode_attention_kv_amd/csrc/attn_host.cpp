@@ -110,10 +110,14 @@ int attn_decode_plan(const attn_shape_t* shape, const int32_t* seqlens_host, int
     m.wgs_per_cu = kc.wgs_per_cu;
     ct = max_tiles;
     double best = m.eval(ct);
-    // candidate chunk lengths: every tile count that changes some split count
-    for (int64_t c = max_tiles - 1; c >= 1; --c) {
-      if (ceil_div(max_tiles, c) == ceil_div(max_tiles, c + 1) && c > 64) continue;
-      double v = m.eval(c);
+    // candidate chunk lengths: the shortest chunk giving the longest sequence
+    // n splits, for every n (about 2 sqrt(max_tiles) distinct values)
+    int64_t prev = max_tiles;
+    for (int64_t n = 2; n <= max_tiles; ++n) {
+      const int64_t c = ceil_div(max_tiles, n);
+      if (c == prev) continue;
+      prev = c;
+      const double v = m.eval(c);
       if (v < best * 0.999) { best = v; ct = c; }
     }
   }

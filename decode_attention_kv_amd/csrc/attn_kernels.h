@@ -30,9 +30,24 @@ inline int narrow_stage_bytes(int kind, int head_dim, int d_rope) {
   return kNarrowWaves * 16 * per_key;
 }
 
+// Environment overrides (read once): ATTN_NARROW_STAGES sets the ring depth,
+// ATTN_FORCE_GENERAL=1 routes every call to the general kernel.
+inline int env_int(const char* name, int dflt) {
+  const char* e = std::getenv(name);
+  return e ? std::atoi(e) : dflt;
+}
+inline int env_stages() {
+  static const int v = env_int("ATTN_NARROW_STAGES", 0);
+  return v;
+}
+inline bool env_force_general() {
+  static const bool v = env_int("ATTN_FORCE_GENERAL", 0) != 0;
+  return v;
+}
+
 inline int narrow_stages(int kind, int head_dim, int d_rope) {
   int s = kNarrowStageTarget / narrow_stage_bytes(kind, head_dim, d_rope);
-  if (const char* e = std::getenv("ATTN_NARROW_STAGES")) s = std::atoi(e);
+  if (env_stages() > 0) s = env_stages();
   return s < 2 ? 2 : s > 6 ? 6 : s;
 }
 
@@ -46,9 +61,7 @@ inline KernelChoice choose_kernel(const attn_shape_t& sh) {
   bool narrow = sh.dtype == ATTN_BF16 && k.rows <= 64 && sh.page_size >= kTile &&
                 ((sh.kind == ATTN_KIND_GQA && (sh.head_dim == 64 || sh.head_dim == 128)) ||
                  (sh.kind == ATTN_KIND_GTA && sh.head_dim == 128 && sh.d_rope == 64));
-  if (const char* e = std::getenv("ATTN_FORCE_GENERAL")) {
-    if (std::atoi(e)) narrow = false;
-  }
+  if (env_force_general()) narrow = false;
   k.narrow = narrow;
   if (narrow) {
     k.stages = narrow_stages(sh.kind, sh.head_dim, sh.d_rope);
