@@ -172,10 +172,8 @@ int attn_decode_plan(const attn_shape_t* shape, const int32_t* seqlens_host, int
 }
 
 size_t attn_decode_workspace_size(const attn_plan_t* plan, int h_q, int d_v) {
-  if (!plan || h_q <= 0 || d_v <= 0) return 0;
-  const size_t rows = (size_t)plan->n_partial_slots * plan->q_len * h_q;
-  const size_t o_bytes = (rows * d_v * 4 + 255) / 256 * 256;
-  return rows ? o_bytes + rows * 4 : 0;
+  if (!plan || h_q <= 0 || d_v <= 0 || plan->n_items <= 0) return 0;
+  return attn_internal::flags_offset(plan, h_q, d_v) + attn_internal::flags_bytes(plan, h_q);
 }
 
 int attn_paged_kv_check(const attn_paged_kv_t* kv) {

@@ -61,8 +61,18 @@ inline KernelChoice choose_kernel(const attn_shape_t& sh) {
   bool narrow = sh.dtype == ATTN_BF16 && k.rows <= 64 && sh.page_size >= kTile &&
                 ((sh.kind == ATTN_KIND_GQA && (sh.head_dim == 64 || sh.head_dim == 128)) ||
                  (sh.kind == ATTN_KIND_GTA && sh.head_dim == 128 && sh.d_rope == 64));
+  // latent heads: the wide streaming kernel (reported through `narrow` too:
+  // "streaming" rather than the general kernel)
+  const bool wide = sh.dtype == ATTN_BF16 && sh.kind == ATTN_KIND_LATENT &&
+                    sh.page_size >= kTile && sh.d_rope == 64 &&
+                    (sh.head_dim == 512 || sh.head_dim == 256);
   if (env_force_general()) narrow = false;
-  k.narrow = narrow;
+  k.narrow = narrow || (wide && !env_force_general());
+  if (k.narrow && sh.kind == ATTN_KIND_LATENT) {
+    k.stages = sh.head_dim >= 512 ? 2 : 3;
+    k.wgs_per_cu = 1;
+    return k;
+  }
   if (narrow) {
     k.stages = narrow_stages(sh.kind, sh.head_dim, sh.d_rope);
     const int lds = k.stages * narrow_stage_bytes(sh.kind, sh.head_dim, sh.d_rope) + 2048;
@@ -73,6 +83,20 @@ inline KernelChoice choose_kernel(const attn_shape_t& sh) {
     k.wgs_per_cu = 1;
   }
   return k;
+}
+
+// Workspace layout: fp32 O_part [slots][q_len][h_q][d_v] (256-byte padded),
+// fp32 LSE_part [slots][q_len][h_q] (256-byte padded), then one int32 flag
+// per workgroup of the latent streaming kernel (its grid is the items padded
+// to a multiple of 8 times at most ceil(rows / 64) row blocks).
+inline size_t flags_offset(const attn_plan_t* plan, int h_q, int d_v) {
+  const size_t rows = (size_t)plan->n_partial_slots * plan->q_len * h_q;
+  return (rows * d_v * 4 + 255) / 256 * 256 + (rows * 4 + 255) / 256 * 256;
+}
+inline size_t flags_bytes(const attn_plan_t* plan, int h_q) {
+  const int64_t rows = (int64_t)(plan->n_groups > 0 ? h_q / plan->n_groups : 0) * plan->q_len;
+  const int64_t blocks = (plan->n_items + 7) / 8 * 8 * ((rows + 63) / 64 > 0 ? (rows + 63) / 64 : 1);
+  return (size_t)blocks * 4;
 }
 
 }  // namespace attn_internal

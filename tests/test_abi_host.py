@@ -124,15 +124,27 @@ def test_plan_errors():
     assert st == binding.ATTN_ERR_INVALID_ARG
 
 
+def _ws_expect(plan, slots, h_q, d_v):
+    rows = slots * plan.q_len * h_q
+    pad = lambda x: (x + 255) // 256 * 256
+    group_rows = h_q // plan.n_groups * plan.q_len
+    flags = (plan.n_items + 7) // 8 * 8 * max(1, -(-group_rows // 64)) * 4
+    return pad(rows * d_v * 4) + pad(rows * 4) + flags
+
+
 def test_workspace_size():
     st, plan, _, info = _plan([5000, 100], chunk=64)
     slots = int(info[info[:, 0] > 1, 0].sum())
-    rows = slots * 1 * 32
-    expect = (rows * 128 * 4 + 255) // 256 * 256 + rows * 4
-    assert binding.attn_decode_workspace_size(plan, 32, 128) == expect
+    assert slots == plan.n_partial_slots
+    assert binding.attn_decode_workspace_size(plan, 32, 128) == _ws_expect(plan, slots, 32, 128)
+    # nothing split: only the per-workgroup flags remain
     st, plan, _, _ = _plan([100, 100], chunk=0)
     assert plan.n_partial_slots == 0
-    assert binding.attn_decode_workspace_size(plan, 32, 128) == 0
+    assert binding.attn_decode_workspace_size(plan, 32, 128) == _ws_expect(plan, 0, 32, 128)
+    st, plan, _, _ = _plan([4096] * 4, q_len=4, h_q=128, groups=2, kind="latent", d=256,
+                           d_rope=64, causal=1)
+    assert binding.attn_decode_workspace_size(plan, 128, 256) == _ws_expect(
+        plan, plan.n_partial_slots, 128, 256)
 
 
 def _host_kv(seqlens, table, num_pages, P=64):

@@ -192,3 +192,24 @@ def test_full_size_sampled(name):
     H.compare(o[pick], l[pick], ref, ref_lse, H.value_max(w, inp, pick), f"{name}/full")
     del d, out, lse
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", ["mla", "gla2"])
+def test_scores_far_above_first_tile(name):
+    """Scores that grow by far more than 2^64 (log2 units) after the first
+    64-key tile: the streaming latent kernel must take its second pass with
+    the true maxima and still match the oracle."""
+    w = SMALL[name].with_(batch=2, seqlen_lo=300, seqlen_hi=300, max_seqlen=320,
+                          softmax_scale=1.0)
+    inp = synth.make_inputs(w)
+    # keys of later tokens get a large component along the queries' first axis
+    q = inp["q"].copy()
+    q[..., 0] = 4.0
+    lat = inp["pool0"].copy()
+    for b in range(w.batch):
+        for i in range(300):
+            pg = inp["page_table"][b, i // w.page_size]
+            lat[pg, i % w.page_size, :, 0] = 0.0 if i < 64 else synth.round_bf16(
+                np.array([min(40.0, i / 4.0)], np.float32))[0]
+    inp.update(q=synth.round_bf16(q), pool0=lat)
+    _check(w, inp, f"{name}/far", chunk_tokens=0)
