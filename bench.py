@@ -26,8 +26,14 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
-KERNEL_SRCS = [os.path.join(ROOT, "decode_attention_kv_amd", "csrc", f)
-               for f in ("attn_decode.hip", "attn_kernels.h")]
+CSRC = os.path.join(ROOT, "decode_attention_kv_amd", "csrc")
+# sources that define the decode kernel a workload runs (shared headers + its
+# kernel family); the hash ties committed counter runs to that code
+KERNEL_SRCS = {
+    "narrow": ("attn_device.h", "attn_kernels.h", "attn_narrow.hip"),
+    "wide": ("attn_device.h", "attn_kernels.h", "attn_wide.hip"),
+    "general": ("attn_device.h", "attn_kernels.h", "attn_general.hip"),
+}
 DESCRIPTIONS = {
     "gqa_llama8b": "GQA decode, Llama-3-8B layer: bf16, B=32, q_len=1, h_q=32, h_kv=8, d=128, "
                    "seqlen ~ U[1024,8192], page 64, permuted page table",
@@ -69,12 +75,20 @@ def flops(w, seqlens):
     return pairs * w.h_q * per
 
 
-def kernel_sha():
-    """Hash of the kernel sources: counter-based traffic is reported only
-    while it was taken on exactly these sources."""
+def kernel_family(w):
+    if w.kind == "latent" and w.dtype == "bf16" and w.page_size >= 64:
+        return "wide"
+    if w.dtype == "bf16" and w.page_size >= 64:
+        return "narrow"
+    return "general"
+
+
+def kernel_sha(w):
+    """Hash of the sources of the workload's decode kernel: counter-based
+    traffic is reported only while it was taken on exactly these sources."""
     h = hashlib.sha256()
-    for path in KERNEL_SRCS:
-        with open(path, "rb") as f:
+    for name in KERNEL_SRCS[kernel_family(w)]:
+        with open(os.path.join(CSRC, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -284,7 +298,7 @@ def main():
     dec_gbps = kvb / (float(dec_ms.mean()) * 1e-3) / 1e9
     dec_tflops = fl / (float(dec_ms.mean()) * 1e-3) / 1e12
     tokens = B * T
-    sha = kernel_sha()
+    sha = kernel_sha(w)
 
     # output sanity on the last step (the parity tests do the real check)
     torch.cuda.synchronize()

@@ -1,9 +1,12 @@
 """Compile libattn_decode.so (gfx950) in-tree with hipcc.
 
-Sources: csrc/attn_host.cpp (host-only planning and checks) and
-csrc/attn_decode.hip (kernels and launchers).  Packed-fp32 VALU ops are
-disabled for device code.
+Sources: csrc/attn_host.cpp (host-only planning and checks),
+csrc/attn_decode.hip (entry points, merge kernel) and one translation unit
+per decode kernel family (attn_general.hip, attn_narrow.hip,
+attn_wide.hip), compiled in parallel.  Packed-fp32 VALU ops are disabled
+for device code.
 """
+import concurrent.futures
 import os
 import subprocess
 import sys
@@ -13,6 +16,8 @@ ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libattn_decode.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
+SOURCES = ("attn_host.cpp", "attn_decode.hip", "attn_general.hip", "attn_narrow.hip",
+           "attn_wide.hip")
 
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-I" + os.path.join(ROOT, "include"),
@@ -33,13 +38,16 @@ def _run(cmd, verbose):
 def build(verbose: bool = True) -> str:
     bdir = os.path.join(ROOT, "_build")
     os.makedirs(bdir, exist_ok=True)
-    objs = []
-    for src in ("attn_host.cpp", "attn_decode.hip"):
+    cmds, objs = [], []
+    for src in SOURCES:
         obj = os.path.join(bdir, src + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        _run([HIPCC] + COMMON + DEVICE_FLAGS + lang + ["-c", os.path.join(PKG, "csrc", src),
-                                                       "-o", obj], verbose)
+        cmds.append([HIPCC] + COMMON + DEVICE_FLAGS + lang +
+                    ["-c", os.path.join(PKG, "csrc", src), "-o", obj])
         objs.append(obj)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(cmds)) as ex:
+        for f in [ex.submit(_run, c, verbose) for c in cmds]:
+            f.result()
     tmp = LIB + ".tmp"
     _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs, verbose)
     os.replace(tmp, LIB)

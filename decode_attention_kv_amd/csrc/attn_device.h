@@ -1,0 +1,111 @@
+// Device-side definitions shared by the decode kernels: vector types, the
+// launch parameter block, small wave-level helpers, and the launchers each
+// kernel translation unit exports to the entry points.
+#ifndef ATTN_DEVICE_H
+#define ATTN_DEVICE_H
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <type_traits>
+
+#include "attn_decode.h"
+#include "attn_kernels.h"
+
+namespace attn_dev {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16;
+
+constexpr int KT = 64;  // keys per tile
+constexpr int kMaxRope = 64;
+
+enum Kind { GQA = 0, GTA = 1, LAT = 2 };
+
+struct Params {
+  const char* pool0;
+  const char* pool1;
+  const char* rope;
+  const int32_t* page_table;
+  int64_t page_stride, token_stride, head_stride;     // elements
+  int64_t rpage_stride, rtoken_stride, rhead_stride;  // elements
+  int32_t max_pages;
+  int32_t page_shift;
+  const void* q;
+  void* out;
+  float* lse;
+  float* o_part;
+  float* lse_part;
+  int32_t* flags;     // latent streaming kernel: per-workgroup fix-up flags
+  const int32_t* items;
+  const int32_t* seqinfo;
+  int32_t q_len, h_q, g, rows;  // rows = g * q_len per group
+  int32_t n_items, row_blocks;
+  int32_t causal;
+  int32_t rope_on;  // GTA: rotate the key's and query's RoPE slices in-kernel
+  float scale_log2;
+  // RoPE: revolutions per position of frequency k as hi + lo floats
+  float rope_hi[kMaxRope / 2];
+  float rope_lo[kMaxRope / 2];
+};
+
+template <typename T> struct DT;
+template <> struct DT<__bf16> { static constexpr int EPC = 8; };   // elements per 16 B
+template <> struct DT<float> { static constexpr int EPC = 4; };
+
+__device__ __forceinline__ float wave_max4(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+__device__ __forceinline__ float wave_sum4(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+// sin/cos of 2*pi*(pos * f) with f = hi + lo, reducing the angle exactly
+// enough for positions up to 2^24.
+__device__ __forceinline__ void rope_sincos(float pos, float hi, float lo, float& s, float& c) {
+  float p = pos * hi;
+  float e = fmaf(pos, hi, -p);
+  float r = p - floorf(p);
+  r += fmaf(pos, lo, e);
+  r -= floorf(r);
+  s = __builtin_amdgcn_sinf(r);
+  c = __builtin_amdgcn_cosf(r);
+}
+
+
+// Scalar (SMEM) load of one int32 from a wave-uniform address, waited for in
+// the same asm block.  SMEM loads count on lgkmcnt, so looking up a page id
+// does not drain the vmcnt-tracked direct-to-LDS loads in flight.
+__device__ __forceinline__ int sload_i32(const int32_t* ptr) {
+  // the address is wave-uniform; readfirstlane makes that explicit so the
+  // operand is allocated to SGPRs
+  const uint64_t a = reinterpret_cast<uint64_t>(ptr);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const int32_t* up = reinterpret_cast<const int32_t*>(((uint64_t)hi << 32) | lo);
+  int v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(up));
+  return v;
+}
+
+// Launchers, one per kernel family (each in its own translation unit).
+// They set the grid-dependent fields of a copy of `p` and enqueue on `stream`.
+// General kernel: every kind / dtype / width the entry points accept.
+int run_general(int kind, bool bf16, int w0, const Params& p, int n_items, hipStream_t stream);
+// Streaming GQA / GTA kernel (bf16, pages >= 64 tokens, <= 64 rows per group).
+int run_narrow(int kind, int d, const Params& p, int n_items, int groups, int stages,
+               hipStream_t stream);
+// Streaming latent kernel (bf16, pages >= 64 tokens, d_c 256 or 512, d_r 64).
+int run_wide(int d_c, const Params& p, int n_items, hipStream_t stream);
+
+}  // namespace attn_dev
+
+#endif  // ATTN_DEVICE_H

@@ -1,0 +1,626 @@
+// Streaming decode kernel for narrow groups (GQA, GTA) on gfx950.
+#include "attn_device.h"
+
+namespace attn_dev {
+namespace {
+
+// ----------------------------------------------------------------------------
+// Streaming kernel for narrow groups (GQA, GTA; at most 16*RT query rows per
+// group, bf16, pages of >= 64 tokens).
+//
+// Four waves share one work item and split every 64-key tile: wave w owns
+// keys [16w, 16w + 16).  Each wave streams its slices through a private ring
+// of STAGES LDS buffers filled by direct global->LDS 16-byte loads, so a wave
+// waits only on its own loads (vmcnt) and the main loop has no barriers.
+// Rows are stored with 16-byte chunks XOR-swizzled by the key index so the
+// K-operand reads of 16 keys and the transposing V reads hit distinct banks.
+// Per 16-key slice: S^T = K Q^T (MFMA 16x16x32), online softmax, and
+// O^T += V^T P^T with MFMA 16x16x16 whose V^T operand comes from
+// ds_read_b64_tr_b16.  The waves' (max, sum, O) states are merged through
+// LDS at the end of the item.
+namespace narrow {
+
+constexpr int NW = 4;    // waves per workgroup
+constexpr int KW = 16;   // keys per wave per tile
+constexpr int KTILE = NW * KW;
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
+
+// N transposing LDS reads (ds_read_b64_tr_b16) in one asm block that also
+// waits for them.  The compiler cannot relate this instruction to the
+// direct-to-LDS loads in flight and would otherwise drain vmcnt before it;
+// here the caller's own vmcnt wait already covers the stage being read.
+typedef unsigned long long u64_t;
+template <int N>
+__device__ __forceinline__ void tr_reads(const uint32_t (&addr)[N], u64_t (&out)[N]);
+template <>
+__device__ __forceinline__ void tr_reads<8>(const uint32_t (&a)[8], u64_t (&o)[8]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %9\n\t"
+      "ds_read_b64_tr_b16 %2, %10\n\t"
+      "ds_read_b64_tr_b16 %3, %11\n\t"
+      "ds_read_b64_tr_b16 %4, %12\n\t"
+      "ds_read_b64_tr_b16 %5, %13\n\t"
+      "ds_read_b64_tr_b16 %6, %14\n\t"
+      "ds_read_b64_tr_b16 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]),
+        "=&v"(o[6]), "=&v"(o[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]),
+        "v"(a[7]));
+}
+template <>
+__device__ __forceinline__ void tr_reads<4>(const uint32_t (&a)[4], u64_t (&o)[4]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4\n\t"
+      "ds_read_b64_tr_b16 %1, %5\n\t"
+      "ds_read_b64_tr_b16 %2, %6\n\t"
+      "ds_read_b64_tr_b16 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]));
+}
+
+// N 16-byte LDS reads in one asm block that also waits for them (same
+// reason as tr_reads: keep the compiler from draining the DMA pipeline).
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+template <int N>
+__device__ __forceinline__ void b128_reads(const uint32_t (&addr)[N], u32x4_t (&out)[N]);
+template <>
+__device__ __forceinline__ void b128_reads<4>(const uint32_t (&a)[4], u32x4_t (&o)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %5\n\t"
+      "ds_read_b128 %2, %6\n\t"
+      "ds_read_b128 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]));
+}
+template <>
+__device__ __forceinline__ void b128_reads<2>(const uint32_t (&a)[2], u32x4_t (&o)[2]) {
+  asm volatile(
+      "ds_read_b128 %0, %2\n\t"
+      "ds_read_b128 %1, %3\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1])
+      : "v"(a[0]), "v"(a[1]));
+}
+
+// All LDS operand reads of one 16-key slice in a single asm block with one
+// wait: NK 16-byte K-operand reads and NV transposing V reads.
+template <int NK, int NV>
+__device__ __forceinline__ void slice_reads(const uint32_t (&ka)[NK], const uint32_t (&va)[NV],
+                                            u32x4_t (&ko)[NK], u64_t (&vo)[NV]);
+template <>
+__device__ __forceinline__ void slice_reads<4, 8>(const uint32_t (&ka)[4], const uint32_t (&va)[8],
+                                                  u32x4_t (&ko)[4], u64_t (&vo)[8]) {
+  asm volatile(
+      "ds_read_b128 %0, %12\n\t"
+      "ds_read_b128 %1, %13\n\t"
+      "ds_read_b128 %2, %14\n\t"
+      "ds_read_b128 %3, %15\n\t"
+      "ds_read_b64_tr_b16 %4, %16\n\t"
+      "ds_read_b64_tr_b16 %5, %17\n\t"
+      "ds_read_b64_tr_b16 %6, %18\n\t"
+      "ds_read_b64_tr_b16 %7, %19\n\t"
+      "ds_read_b64_tr_b16 %8, %20\n\t"
+      "ds_read_b64_tr_b16 %9, %21\n\t"
+      "ds_read_b64_tr_b16 %10, %22\n\t"
+      "ds_read_b64_tr_b16 %11, %23\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(ko[0]), "=&v"(ko[1]), "=&v"(ko[2]), "=&v"(ko[3]), "=&v"(vo[0]), "=&v"(vo[1]),
+        "=&v"(vo[2]), "=&v"(vo[3]), "=&v"(vo[4]), "=&v"(vo[5]), "=&v"(vo[6]), "=&v"(vo[7])
+      : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "v"(va[0]), "v"(va[1]), "v"(va[2]),
+        "v"(va[3]), "v"(va[4]), "v"(va[5]), "v"(va[6]), "v"(va[7]));
+}
+template <>
+__device__ __forceinline__ void slice_reads<2, 4>(const uint32_t (&ka)[2], const uint32_t (&va)[4],
+                                                  u32x4_t (&ko)[2], u64_t (&vo)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %6\n\t"
+      "ds_read_b128 %1, %7\n\t"
+      "ds_read_b64_tr_b16 %2, %8\n\t"
+      "ds_read_b64_tr_b16 %3, %9\n\t"
+      "ds_read_b64_tr_b16 %4, %10\n\t"
+      "ds_read_b64_tr_b16 %5, %11\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(ko[0]), "=&v"(ko[1]), "=&v"(vo[0]), "=&v"(vo[1]), "=&v"(vo[2]), "=&v"(vo[3])
+      : "v"(ka[0]), "v"(ka[1]), "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3]));
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)(p);
+}
+
+template <int KIND, int D, int DR> struct Geo {
+  // per-wave bytes of one stage: K (or tied) rows, V rows (GQA), RoPE rows (GTA)
+  static constexpr int ROW0 = D * 2;                 // K / tied row bytes
+  static constexpr int ROWR = DR * 2;                // RoPE row bytes
+  static constexpr int K_OFF = 0;
+  static constexpr int V_OFF = KW * ROW0;            // GQA only
+  static constexpr int R_OFF = KW * ROW0;            // GTA only
+  static constexpr int WAVE_BYTES = (KIND == GQA) ? 2 * KW * ROW0 : KW * (ROW0 + ROWR);
+  static constexpr int STAGE_BYTES = NW * WAVE_BYTES;
+  static constexpr int LOADS = (KIND == GQA) ? 2 * KW * ROW0 / 1024 : KW * (ROW0 + ROWR) / 1024;
+};
+
+// Per-lane byte offsets of the direct-to-LDS loads of one 16-key slice of
+// rows of ROWB bytes: lane l of load i covers row i*RPI + l/CPR at swizzled
+// chunk position l%CPR, i.e. it fetches logical chunk (l%CPR) ^ (row % CPR).
+template <int ROWB>
+struct SliceDMA {
+  static constexpr int CPR = ROWB / 16;  // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;   // rows per 1 KB load
+  static constexpr int N = KW / RPI;     // loads per slice
+  uint32_t off[N];                       // bytes from the slice's first row
+  int row[N];
+  __device__ __forceinline__ void init(int64_t token_stride, int lane) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      row[i] = i * RPI + lane / CPR;
+      const int c = (lane % CPR) ^ (row[i] & (CPR - 1));
+      off[i] = (uint32_t)(row[i] * token_stride * 2 + c * 16);
+    }
+  }
+  // full slice: every row valid, contiguous within one page
+  __device__ __forceinline__ void issue(char* dst, const char* base) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(base + off[i]), (lds_void_t*)(dst + i * 1024),
+                                       16, 0, 0);
+  }
+  // partial slice: rows at or past `valid` re-read row valid-1 (same page)
+  __device__ __forceinline__ void issue_clamped(char* dst, const char* base, int valid,
+                                                int64_t token_stride) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int r = min(row[i], valid - 1);
+      const char* src = base + off[i] + (int64_t)(r - row[i]) * token_stride * 2;
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(dst + i * 1024), 16, 0, 0);
+    }
+  }
+};
+
+template <int KIND, int D, int DR, int RT, int STAGES>
+__global__ __launch_bounds__(NW * 64) void decode_narrow(Params p) {
+  using G = Geo<KIND, D, DR>;
+  constexpr int DN = D - DR;          // key entries from the K / tied row
+  constexpr int NKC = D / 32;         // 32-dim k-chunks of the score MFMA
+  constexpr int NDVT = D / 16;        // 16-wide output tiles
+  constexpr int CPR0 = G::ROW0 / 16;
+  constexpr int CPRR = (DR > 0) ? G::ROWR / 16 : 1;
+  static_assert(STAGES >= 2 && STAGES <= 6, "stages");
+  static_assert(G::LOADS * 1024 == G::WAVE_BYTES, "whole 1 KB load instructions");
+
+  __shared__ __attribute__((aligned(1024))) char st0[G::STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char st1[G::STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char st2[STAGES > 2 ? G::STAGE_BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) char st3[STAGES > 3 ? G::STAGE_BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) char st4[STAGES > 4 ? G::STAGE_BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) char st5[STAGES > 5 ? G::STAGE_BYTES : 16];
+  __shared__ float merge_m[NW][16 * RT], merge_l[NW][16 * RT];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+
+  // Workgroups are dealt round-robin to the 8 XCDs (block i -> XCD i % 8).
+  // The plan lists the groups of one (sequence, chunk) consecutively; they
+  // are mapped to blocks 8 apart so they share one XCD's L2 (GTA's RoPE key
+  // rows are read by every group).
+  const int gsz = p.row_blocks;  // groups per (sequence, chunk)
+  const int bid = blockIdx.x;
+  const int blk = bid / (8 * gsz);
+  const int rem = bid - blk * 8 * gsz;
+  const int item = (blk * 8 + (rem & 7)) * gsz + (rem >> 3);
+  if (item >= p.n_items) return;
+  const int32_t* it = p.items + 4 * item;
+  const int b = __builtin_amdgcn_readfirstlane(it[0]);
+  const int j = __builtin_amdgcn_readfirstlane(it[1]);
+  const int split = __builtin_amdgcn_readfirstlane(it[2]);
+  const int t0 = __builtin_amdgcn_readfirstlane(it[3]);
+  const int32_t* si = p.seqinfo + 4 * b;
+  const int n_splits = __builtin_amdgcn_readfirstlane(si[0]);
+  const int slot_base = __builtin_amdgcn_readfirstlane(si[1]);
+  const int L = __builtin_amdgcn_readfirstlane(si[2]);
+  const int chunk = __builtin_amdgcn_readfirstlane(si[3]);
+  const int t_end = min(t0 + chunk, L);
+  const int n_tiles = (t_end - t0 + KTILE - 1) / KTILE;
+  const int t_last = t_end - 1;
+  const int pmask = (1 << p.page_shift) - 1;
+  const int32_t* pt_row = p.page_table + (int64_t)b * p.max_pages;
+
+  // rows of this lane (every wave holds every row)
+  int tq[RT], hq[RT], qlimit[RT];
+  bool row_ok[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int row = rt * 16 + col;
+    row_ok[rt] = row < p.rows;
+    tq[rt] = row_ok[rt] ? row / p.g : 0;
+    hq[rt] = j * p.g + (row_ok[rt] ? row - tq[rt] * p.g : 0);
+    qlimit[rt] = (p.causal && row_ok[rt]) ? L - p.q_len + tq[rt] : 0x7fffffff;
+  }
+
+  auto stage = [&](int u) -> char* {
+    switch (u) {
+      case 0: return st0;
+      case 1: return st1;
+      case 2: return st2;
+      case 3: return st3;
+      case 4: return st4;
+      default: return st5;
+    }
+  };
+
+  // direct-to-LDS load offsets of this lane (loop invariant)
+  SliceDMA<G::ROW0> dma0;
+  SliceDMA<(DR > 0 ? G::ROWR : 16)> dmar;
+  dma0.init(p.token_stride, lane);
+  if constexpr (KIND == GTA) dmar.init(p.rtoken_stride, lane);
+
+  // issue this wave's loads of tile `t` (clamped to the last tile) into stage u
+  auto issue = [&](int t, int u) {
+    const int tt = min(t, n_tiles - 1);
+    const int key0 = t0 + tt * KTILE + wave * KW;   // 16-aligned, inside one page
+    const int kc = min(key0, t_last);
+    const int valid = t_last - kc + 1;              // rows of the slice that exist
+    const int64_t page = sload_i32(pt_row + (kc >> p.page_shift));
+    const int slot0 = kc & pmask & ~(KW - 1);       // first row of the slice in its page
+    char* dst = stage(u) + wave * G::WAVE_BYTES;
+    const int64_t row0 = page * p.page_stride + (int64_t)slot0 * p.token_stride +
+                         (int64_t)j * p.head_stride;
+    const char* b0 = p.pool0 + row0 * 2;
+    // rows past the chunk's end re-read its last row (for a slice wholly
+    // past the end, kc is that row and slot0 its 16-aligned block)
+    const int v = min((key0 <= t_last) ? valid : ((kc & pmask) - slot0 + 1), KW);
+    dma0.issue_clamped(dst + G::K_OFF, b0, v, p.token_stride);
+    if constexpr (KIND == GQA) {
+      dma0.issue_clamped(dst + G::V_OFF, p.pool1 + row0 * 2, v, p.token_stride);
+    } else {
+      dmar.issue_clamped(dst + G::R_OFF,
+                         p.rope + (page * p.rpage_stride + (int64_t)slot0 * p.rtoken_stride) * 2,
+                         v, p.rtoken_stride);
+    }
+  };
+
+  // RoPE frequencies of this lane's 8 pairs (entries 8 grp + u), hoisted so
+  // no per-lane kernel-argument loads sit inside the streaming loop
+  float rh[8], rl[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    rh[u] = (KIND == GTA) ? p.rope_hi[grp * 8 + u] : 0.f;
+    rl[u] = (KIND == GTA) ? p.rope_lo[grp * 8 + u] : 0.f;
+  }
+
+  // ---- query B operands in registers (rotated for GTA)
+  bf16x8 qreg[RT][NKC];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const __bf16* qrow = reinterpret_cast<const __bf16*>(p.q) +
+                         ((int64_t)(b * p.q_len + tq[rt]) * p.h_q + hq[rt]) * D;
+#pragma unroll
+    for (int c = 0; c < NKC; ++c) {
+      uint4 raw = make_uint4(0u, 0u, 0u, 0u);
+      if (row_ok[rt]) raw = *reinterpret_cast<const uint4*>(qrow + c * 32 + grp * 8);
+      qreg[rt][c] = __builtin_bit_cast(bf16x8, raw);
+    }
+    if constexpr (KIND == GTA) {
+      if (p.rope_on) {
+        constexpr int c0 = DN / 32;
+        const float qpos = (float)(L - p.q_len + tq[rt]);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          float sn, cs;
+          rope_sincos(qpos, rh[u], rl[u], sn, cs);
+          const float x = (float)qreg[rt][c0][u], y = (float)qreg[rt][c0 + 1][u];
+          qreg[rt][c0][u] = (__bf16)(x * cs - y * sn);
+          qreg[rt][c0 + 1][u] = (__bf16)(x * sn + y * cs);
+        }
+      }
+    }
+  }
+
+  f32x4 acc[RT][NDVT];
+  float m_run[RT], l_run[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    m_run[rt] = -INFINITY;
+    l_run[rt] = 0.f;
+#pragma unroll
+    for (int i = 0; i < NDVT; ++i) acc[rt][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // start the ring; then wait for the (older) query loads only, so no
+  // query load is still pending when the streaming loop starts
+  if (n_tiles > 0) {
+#pragma unroll
+    for (int u = 0; u < STAGES - 1; ++u) issue(u, u);
+  }
+  {
+    constexpr int ahead = (STAGES - 1) * G::LOADS;
+    __builtin_amdgcn_s_waitcnt((ahead & 15) | ((ahead >> 4) << 14) | (0x7 << 4) | (0xf << 8));
+  }
+
+  // byte offsets (within a wave's V rows) of this lane's transposing reads:
+  // lane `col` of group `grp` addresses key row 4 grp + col/4 and the
+  // 4-column group (col % 4) of each 16-wide output tile, whose 16-byte chunk
+  // sits at its XOR-swizzled position
+  uint32_t v_off[NDVT];
+  {
+    const int kl = grp * 4 + (col >> 2);
+    const int sw = kl & (CPR0 - 1);
+#pragma unroll
+    for (int dt = 0; dt < NDVT; ++dt) {
+      const int cidx = 2 * dt + ((col & 3) >> 1);
+      v_off[dt] = kl * G::ROW0 + ((cidx ^ sw) * 16) + (col & 1) * 8;
+    }
+  }
+
+  // byte offsets (within a wave's stage) of this lane's K-operand chunks
+  uint32_t k_off[NKC];
+#pragma unroll
+  for (int c = 0; c < NKC; ++c) {
+    const int ch = 4 * c + grp;
+    k_off[c] = (KIND == GQA || ch < DN / 8)
+                   ? G::K_OFF + col * G::ROW0 + ((ch ^ (col & (CPR0 - 1))) * 16)
+                   : G::R_OFF + col * G::ROWR + (((ch - DN / 8) ^ (col & (CPRR - 1))) * 16);
+  }
+
+  // one 16-key slice of tile t, read from stage u
+  auto compute = [&](int t, int u) {
+    const char* sb = stage(u) + wave * G::WAVE_BYTES;
+    const int key0 = t0 + t * KTILE + wave * KW;
+    // scores
+    f32x4 sa[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) sa[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // all operand reads of the slice: K chunks (8 dims 32c + 8 grp .. of
+    // key `col`) and the V^T tiles, one LDS round trip
+    u32x4_t kraw[NKC];
+    u64_t vraw[NDVT];
+    {
+      const uint32_t sbase = lds_addr(sb);
+      const uint32_t vbase = sbase + ((KIND == GQA) ? G::V_OFF : G::K_OFF);
+      uint32_t ka_addr[NKC], va_addr[NDVT];
+#pragma unroll
+      for (int c = 0; c < NKC; ++c) ka_addr[c] = sbase + k_off[c];
+#pragma unroll
+      for (int dt = 0; dt < NDVT; ++dt) va_addr[dt] = vbase + v_off[dt];
+      slice_reads<NKC, NDVT>(ka_addr, va_addr, kraw, vraw);
+    }
+    auto kread = [&](int c) { return __builtin_bit_cast(bf16x8, kraw[c]); };
+    auto mma = [&](bf16x8 a, int c) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+        sa[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[rt][c], sa[rt], 0, 0, 0);
+    };
+    if constexpr (KIND == GTA) {
+      constexpr int c0 = DN / 32;
+#pragma unroll
+      for (int c = 0; c < c0; ++c) mma(kread(c), c);
+      bf16x8 ka = kread(c0), kb = kread(c0 + 1);
+      if (p.rope_on) {
+        const float kpos = (float)(key0 + col);
+#pragma unroll
+        for (int u2 = 0; u2 < 8; ++u2) {
+          float sn, cs;
+          rope_sincos(kpos, rh[u2], rl[u2], sn, cs);
+          const float x = (float)ka[u2], y = (float)kb[u2];
+          ka[u2] = (__bf16)(x * cs - y * sn);
+          kb[u2] = (__bf16)(x * sn + y * cs);
+        }
+      }
+      mma(ka, c0);
+      mma(kb, c0 + 1);
+#pragma unroll
+      for (int c = c0 + 2; c < NKC; ++c) mma(kread(c), c);
+    } else {
+#pragma unroll
+      for (int c = 0; c < NKC; ++c) mma(kread(c), c);
+    }
+    // mask + online softmax; lane holds keys key0 + 4 grp + i of its rows.
+    // The running max is only raised (and O, l rescaled) when a row's max
+    // grows by more than 2^8: probabilities then stay below 256, harmless in
+    // fp32 and bf16, and most slices skip the rescale of the accumulators.
+    const bool full = (key0 + KW <= t_end) && !p.causal;
+    float s[RT][4];
+    bool any_raise = false;
+    float m_upd[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float v = sa[rt][i] * p.scale_log2;
+        if (!full) {
+          const int key = key0 + grp * 4 + i;
+          v = (key < t_end && key <= qlimit[rt]) ? v : -INFINITY;
+        }
+        s[rt][i] = v;
+        tmax = fmaxf(tmax, v);
+      }
+      tmax = wave_max4(tmax);
+      const bool raise = tmax > m_run[rt] + 8.f;
+      m_upd[rt] = raise ? tmax : m_run[rt];
+      any_raise |= raise;
+    }
+    if (__builtin_amdgcn_ballot_w64(any_raise) != 0) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const float alpha = __builtin_amdgcn_exp2f(m_run[rt] - m_upd[rt]);
+        if (m_upd[rt] != m_run[rt]) {
+          l_run[rt] *= alpha;
+        }
+        const float a = (m_upd[rt] != m_run[rt]) ? alpha : 1.f;
+#pragma unroll
+        for (int dt = 0; dt < NDVT; ++dt) acc[rt][dt] *= a;
+        m_run[rt] = m_upd[rt];
+      }
+    }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const float m_use = (m_run[rt] == -INFINITY) ? 0.f : m_run[rt];
+      float psum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s[rt][i] = __builtin_amdgcn_exp2f(s[rt][i] - m_use);
+        psum += s[rt][i];
+      }
+      l_run[rt] += psum;
+    }
+    // O^T += V^T P^T (k = this wave's 16 keys; lane group g holds keys 4g..4g+3)
+    bf16x4 pb[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pb[rt][i] = (__bf16)s[rt][i];
+#pragma unroll
+    for (int dt = 0; dt < NDVT; ++dt) {
+      const bf16x4 va = __builtin_bit_cast(bf16x4, vraw[dt]);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+        acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb[rt], acc[rt][dt], 0, 0, 0);
+    }
+  };
+
+  // ---- main loop, unrolled by STAGES so every stage is a distinct LDS object
+  for (int t = 0; t < n_tiles; t += STAGES) {
+#pragma unroll
+    for (int u = 0; u < STAGES; ++u) {
+      if (t + u < n_tiles) {
+        // every wave has read stage (u-1) of the previous tile before reuse
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+        issue(t + u + STAGES - 1, (u + STAGES - 1) % STAGES);
+        // wait until this tile's loads (issued STAGES-1 tiles ago) landed
+        constexpr int ahead = (STAGES - 1) * G::LOADS;
+        __builtin_amdgcn_s_waitcnt((ahead & 15) | ((ahead >> 4) << 14) | (0x7 << 4) | (0xf << 8));
+        compute(t + u, u);
+      }
+    }
+  }
+
+  // ---- merge the four waves' softmax states through LDS
+  __builtin_amdgcn_s_waitcnt(0);   // drain this wave's clamped trailing loads
+  __syncthreads();
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const float l_w = wave_sum4(l_run[rt]);
+    if (grp == 0) {
+      merge_m[wave][rt * 16 + col] = m_run[rt];
+      merge_l[wave][rt * 16 + col] = l_w;
+    }
+  }
+  __syncthreads();
+  // columns merged per pass: the largest power of two whose four per-wave
+  // 16-row slabs fit one stage buffer
+  constexpr int DP0 = G::STAGE_BYTES / (NW * 16 * 4);
+  constexpr int DP = DP0 >= D ? D : DP0 >= 128 ? 128 : DP0 >= 64 ? 64 : 32;
+  static_assert(D % DP == 0 && DP % (NW * 4) == 0, "merge passes");
+  float* obuf = reinterpret_cast<float*>(st0);  // [NW][16][DP] fp32
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int r = rt * 16 + col;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, merge_m[w][r]);
+    const float mu = (mx == -INFINITY) ? 0.f : mx;
+    float lt = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) lt += merge_l[w][r] * exp2f(merge_m[w][r] - mu);
+    const float sc = exp2f(m_run[rt] - mu);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const float lse_val = lt > 0.f ? (mu + __log2f(lt)) * 0.69314718055994531f : -INFINITY;
+    const int64_t orow = (int64_t)(b * p.q_len + tq[rt]) * p.h_q + hq[rt];
+    const int64_t prow = (int64_t)((slot_base + split) * p.q_len + tq[rt]) * p.h_q + hq[rt];
+#pragma unroll
+    for (int pass = 0; pass < D / DP; ++pass) {
+#pragma unroll
+      for (int dt = pass * (DP / 16); dt < (pass + 1) * (DP / 16); ++dt)
+        *reinterpret_cast<f32x4*>(obuf + ((wave * 16 + col) * DP + dt * 16 - pass * DP + grp * 4)) =
+            acc[rt][dt] * sc;
+      __syncthreads();
+      // each wave finishes DP/NW columns of the 16 rows
+      constexpr int COLS = DP / NW;
+#pragma unroll
+      for (int c4 = grp * 4; c4 < COLS; c4 += 16) {
+        const int cl = wave * COLS + c4;
+        f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < NW; ++w) o += *reinterpret_cast<const f32x4*>(obuf + ((w * 16 + col) * DP + cl));
+        o *= inv;
+        const int dv = pass * DP + cl;
+        if (row_ok[rt]) {
+          if (n_splits <= 1) {
+            __bf16 v4[4] = {(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
+            *reinterpret_cast<uint2*>(reinterpret_cast<__bf16*>(p.out) + orow * D + dv) =
+                __builtin_bit_cast(uint2, v4);
+          } else {
+            *reinterpret_cast<f32x4*>(p.o_part + prow * D + dv) = o;
+          }
+        }
+      }
+      __syncthreads();
+    }
+    if (row_ok[rt] && wave == 0 && grp == 0) {
+      if (n_splits <= 1) {
+        if (p.lse) p.lse[orow] = lse_val;
+      } else {
+        p.lse_part[prow] = lse_val;
+      }
+    }
+  }
+}
+
+}  // namespace narrow
+
+template <int KIND, int D, int DR, int RT, int S>
+int launch_narrow_s(Params p, int n_items, int groups, hipStream_t stream) {
+  using G = narrow::Geo<KIND, D, DR>;
+  if constexpr (S * G::STAGE_BYTES + 4096 > 163840) {
+    return launch_narrow_s<KIND, D, DR, RT, S - 1>(p, n_items, groups, stream);
+  } else {
+    p.n_items = n_items;
+    p.row_blocks = groups;
+    const int blocks = (n_items + 8 * groups - 1) / (8 * groups) * 8 * groups;
+    hipLaunchKernelGGL((narrow::decode_narrow<KIND, D, DR, RT, S>), dim3(blocks),
+                       dim3(narrow::NW * 64), 0, stream, p);
+    return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+  }
+}
+
+template <int KIND, int D, int DR, int RT>
+int launch_narrow_rt(const Params& p, int n_items, int groups, int stages, hipStream_t stream) {
+  switch (stages) {
+    case 2: return launch_narrow_s<KIND, D, DR, RT, 2>(p, n_items, groups, stream);
+    case 3: return launch_narrow_s<KIND, D, DR, RT, 3>(p, n_items, groups, stream);
+    case 4: return launch_narrow_s<KIND, D, DR, RT, 4>(p, n_items, groups, stream);
+    case 5: return launch_narrow_s<KIND, D, DR, RT, 5>(p, n_items, groups, stream);
+    default: return launch_narrow_s<KIND, D, DR, RT, 6>(p, n_items, groups, stream);
+  }
+}
+
+template <int KIND, int D, int DR>
+int launch_narrow(const Params& p, int n_items, int groups, int stages, hipStream_t stream) {
+  const int rt = (p.rows + 15) / 16;
+  if (rt <= 1) return launch_narrow_rt<KIND, D, DR, 1>(p, n_items, groups, stages, stream);
+  if (rt <= 2) return launch_narrow_rt<KIND, D, DR, 2>(p, n_items, groups, stages, stream);
+  return launch_narrow_rt<KIND, D, DR, 4>(p, n_items, groups, stages, stream);
+}
+
+}  // namespace
+
+int run_narrow(int kind, int d, const Params& p, int n_items, int groups, int stages,
+               hipStream_t stream) {
+  if (kind == GTA) return launch_narrow<GTA, 128, 64>(p, n_items, groups, stages, stream);
+  return d == 128 ? launch_narrow<GQA, 128, 0>(p, n_items, groups, stages, stream)
+                  : launch_narrow<GQA, 64, 0>(p, n_items, groups, stages, stream);
+}
+
+}  // namespace attn_dev
