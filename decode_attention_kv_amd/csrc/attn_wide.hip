@@ -1,58 +1,90 @@
 // Streaming decode kernel for latent heads (MLA, GLA) on gfx950.
+//
+// A latent group's keys are [latent_j || RoPE] rows and its values are the
+// latent rows themselves ("Hardware-Efficient Attention for Fast Decoding",
+// Core claim; the MLA and GLA definitions).  One workgroup of four waves
+// holds 32*RT query rows of a group (the group's heads times the query
+// tokens, or a block of them) and streams the rows of its chunk through a
+// ring of STAGES 64-key LDS stages filled by direct global->LDS loads.
+//
+// Work split inside a workgroup: wave (kh, rh) owns the row half rh
+// (16*RT rows) and
+//   * scores S^T = K Q^T for the key half kh of every tile (32 keys; its
+//     rows' queries stay in registers as MFMA B operands),
+//   * O^T += V^T P^T for the value-column half kh of its rows over all 64
+//     keys of the tile; the probabilities of the other key half come from
+//     the partner wave (kh^1, rh) through a small LDS buffer.
+// So every K element is read from LDS by two waves (one per row half) and
+// every V element by two (one per row half), half of what a split over rows
+// alone needs.
+//
+// LDS layout of a stage (64 banks of 4 bytes, 16 lanes served per cycle):
+// the 16-byte K reads of 16 consecutive keys and the transposing V^T reads
+// (4 keys x 2 16-byte units per 16 lanes) must hit distinct banks.  Latent
+// blocks of 1 KB (one 512-wide row, or two 256-wide rows) sit 1072 bytes
+// apart, a stride of 3 mod 16 units, set by the LDS base of each
+// direct-to-LDS load (one 1 KB load per block); within a two-row block the
+// second row's units are XOR-ed with 8.  RoPE rows are 128 bytes, unpadded,
+// with units XOR-ed by (row / 2) mod 8.  Every operand address is then one
+// or two per-lane bases plus an immediate offset, and each load needs a
+// single per-lane offset register.
+//
+// Softmax: every row keeps a fixed reference max m_ref, the pair-wide max
+// of its first tile (the visible keys of a chunk are a prefix of it, so
+// rows with any visible key have one there), and O is never rescaled;
+// probabilities exp2(s - m_ref) are exact until a score exceeds m_ref by
+// 2^64 (log2 units).  A workgroup that sees such a score writes nothing and
+// sets its flag; a second launch redoes exactly those workgroups with the
+// classic online rescaling (RESCALE = true).
 #include "attn_device.h"
 
 namespace attn_dev {
 namespace {
-
-
-// ----------------------------------------------------------------------------
-// Streaming kernel for latent heads (MLA / GLA): wide rows, many query rows.
-//
-// One workgroup holds NW*RT*16 query rows of one latent group (the group's
-// heads times the query tokens, or a block of them) and streams the group's
-// [latent || RoPE key] rows of its chunk through a ring of STAGES 64-key LDS
-// stages shared by all waves.  The ring is filled by direct-to-LDS loads
-// issued from inline asm, so the compiler sees no pending vector loads and
-// schedules the ordinary LDS operand reads with lgkmcnt waits only; one
-// barrier per stage hands the stage from loads to readers.  Every K and V^T
-// operand read from LDS feeds RT MFMAs (one per row tile of the wave).
-// Scores are transposed (S^T = K Q^T, keys on M) so P^T is the B operand of
-// O^T += V^T P^T straight from registers; V^T comes from
-// ds_read_b64_tr_b16.
-#ifndef WIDE_SB_K
-#define WIDE_SB_K 0
-#endif
-#ifndef WIDE_SB_V
-#define WIDE_SB_V 0
-#endif
 namespace wide {
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
 
-// One direct global->LDS 16-byte load per lane: lane l writes LDS bytes
-// [lds + 16 l, lds + 16 l + 16).  Issued from asm so that the compiler
-// does not drain vmcnt before unrelated LDS reads; waits are explicit.
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
-  const uint32_t l = __builtin_amdgcn_readfirstlane(lds);  // wave-uniform LDS base
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(l)
-               : "memory");
-}
+constexpr int NW = 4;  // waves: key half kh = wave & 1, row half rh = wave >> 1
 
 __device__ __forceinline__ uint32_t lds_u32(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)(p);
 }
 
+// A wave-uniform 64-bit pointer, made explicit so it is allocated to SGPRs.
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return reinterpret_cast<const char*>(((uint64_t)hi << 32) | lo);
+}
+
+// One direct global->LDS 16-byte load per lane from base + voff (base in
+// SGPRs, voff a per-lane 32-bit byte offset); lane l writes LDS bytes
+// [lds + 16 l, lds + 16 l + 16).  Issued from asm so that the compiler does
+// not drain vmcnt before unrelated LDS reads; waits are explicit.  The
+// nontemporal hint (nt) suits data read once and raises streaming read
+// bandwidth by about a tenth on gfx950.
+__device__ __forceinline__ void dma16(const char* base, uint32_t voff, uint32_t lds) {
+  const uint32_t l = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt" : : "v"(voff), "s"(base),
+               "s"(l) : "memory");
+}
+
 template <int DC, int DR> struct Geo {
-  static constexpr int LROW = DC * 2;               // latent row bytes
-  static constexpr int RROW = DR * 2;               // RoPE row bytes
-  static constexpr int LCPR = LROW / 16;            // 16-byte chunks per latent row
-  static constexpr int RCPR = RROW / 16;
-  static constexpr int R_OFF = 64 * LROW;           // RoPE block after the latent block
-  static constexpr int STAGE = 64 * (LROW + RROW);
-  static constexpr int LLOADS = 64 * LROW / 1024;   // 1 KB loads per stage
-  static constexpr int RLOADS = 64 * RROW / 1024;
+  static_assert((DC == 256 || DC == 512) && DR == 64, "latent widths");
+  static constexpr bool PAIR = DC == 256;    // two latent rows per 1 KB block
+  static constexpr int BSTR = 1072;          // latent block stride (67 units, 3 mod 16)
+  static constexpr int LLOADS = PAIR ? 32 : 64;   // latent blocks (1 KB loads) per stage
+  static constexpr int R_OFF = LLOADS * BSTR + (PAIR ? 512 : 0);  // 1 KB aligned
+  static constexpr int RLOADS = 8;           // 64 RoPE rows x 128 bytes
   static constexpr int LOADS = LLOADS + RLOADS;
+  static constexpr int STAGE = R_OFF + RLOADS * 1024;
+  static constexpr int NKC = (DC + DR) / 32;  // 32-dim k-chunks of a score
+  static constexpr int NKL = DC / 32;         // ... of which latent
+  static constexpr int NDVH = DC / 32;        // 16-wide value tiles in one half
+  static_assert(LLOADS % NW == 0 && RLOADS % NW == 0, "loads split evenly over the waves");
+  static_assert(R_OFF % 1024 == 0, "RoPE block alignment");
 };
 
 // Per-workgroup context of one work item.
@@ -60,40 +92,26 @@ struct Item {
   int b, j, split, t0, t_end, n_tiles, n_splits, slot_base, L, rblk;
 };
 
-// Stream the item's chunk through the LDS ring and write its output rows.
-//
-// RESCALE = false: each row keeps a FIXED reference max m_ref, the max of
-// its first tile with a visible key (the visible keys of a chunk are a
-// prefix of it, so that is the first tile, while O and l are still zero);
-// O is never rescaled.  Probabilities exp2(s - m_ref) are exact in floating
-// point; while no score exceeds m_ref by more than 2^64 (log2 units) every
-// sum stays far below the fp32 range.  Returns true, without writing
-// anything, if some row of the workgroup exceeded that bound.
-// RESCALE = true: the classic online softmax (the running max is raised and
-// O, l rescaled whenever a tile's max exceeds it); never fails.  It is only
-// called for such rare workgroups, as a separate function so that its
-// register needs do not burden the fixed-reference loop.
-template <int DC, int DR, int NW, int RT, int STAGES, bool RESCALE>
-__device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* ring,
-                                       int* restart_flag) {
+constexpr int PT_MAX = 512;  // tiles whose page ids are kept in LDS
+
+// Stream the item's chunk and write its output rows; returns true, writing
+// nothing, when (RESCALE = false) some row outgrew its fixed reference.
+template <int DC, int DR, int RT, int STAGES, bool RESCALE>
+__device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* ring) {
   using G = Geo<DC, DR>;
-  constexpr int DK = DC + DR;
-  constexpr int NKC = DK / 32;     // 32-dim k-chunks
-  constexpr int NDVT = DC / 16;    // 16-wide output tiles
-  constexpr int ROWS = NW * RT * 16;
-  constexpr int LPW = G::LOADS / NW;  // loads per wave per stage
-  // k-chunks / V^T tiles per scheduling region (0: no fences)
-  constexpr int SB_K = WIDE_SB_K;
-  constexpr int SB_V = WIDE_SB_V;
+  constexpr int LPW = G::LOADS / NW;   // loads per wave per stage
+  constexpr int R_WG = 32 * RT;        // rows per workgroup
+  constexpr int PBUF = STAGES * G::STAGE;
+  constexpr int PTAB = PBUF + 4 * RT * 1024;   // page-id table
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kh = wave & 1, rh = wave >> 1;
   const int col = lane & 15;
   const int grp = lane >> 4;
   const int b = itm.b, j = itm.j, t0 = itm.t0, t_end = itm.t_end, n_tiles = itm.n_tiles;
   const int L = itm.L;
-  const int t_last = t_end - 1;
   const int pmask = (1 << p.page_shift) - 1;
   const int32_t* pt_row = p.page_table + (int64_t)b * p.max_pages;
 
@@ -101,7 +119,7 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
   bool row_ok[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    const int row = itm.rblk * ROWS + (wave * RT + rt) * 16 + col;
+    const int row = itm.rblk * R_WG + (rh * RT + rt) * 16 + col;
     row_ok[rt] = row < p.rows;
     tq[rt] = row_ok[rt] ? row / p.g : 0;
     hq[rt] = j * p.g + (row_ok[rt] ? row - tq[rt] * p.g : 0);
@@ -109,66 +127,135 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
   }
 
   // ---- query B operands: Q^T[k = dims 32c + 8 grp ..][n = row]
-  bf16x8 qreg[RT][NKC];
+  bf16x8 qreg[RT][G::NKC];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const __bf16* qrow = reinterpret_cast<const __bf16*>(p.q) +
-                         ((int64_t)(b * p.q_len + tq[rt]) * p.h_q + hq[rt]) * DK;
+                         ((int64_t)(b * p.q_len + tq[rt]) * p.h_q + hq[rt]) * (DC + DR);
 #pragma unroll
-    for (int c = 0; c < NKC; ++c) {
+    for (int c = 0; c < G::NKC; ++c) {
       uint4 raw = make_uint4(0u, 0u, 0u, 0u);
       if (row_ok[rt]) raw = *reinterpret_cast<const uint4*>(qrow + c * 32 + grp * 8);
       qreg[rt][c] = __builtin_bit_cast(bf16x8, raw);
     }
   }
-  // the query loads must be complete before the asm loads start counting
+
+  // ---- per-lane source offsets of the direct-to-LDS loads.  Latent: a
+  // 1 KB block is one 512-wide row (lane = 16-byte unit) or two 256-wide
+  // rows (lanes 32..63 take the second row, units XOR-ed with 8).  RoPE:
+  // load k covers rows 8k .. 8k + 7 (lane / 8), units XOR-ed with
+  // (row / 2) mod 8, which for this wave's loads depends on wave parity only.
+  const int64_t lts2 = p.token_stride * 2, rts2 = p.rtoken_stride * 2;
+  const int lrow = G::PAIR ? (lane >> 5) : 0;                   // row within the block
+  const int lunit = G::PAIR ? ((lane & 31) ^ (8 * lrow)) : lane;  // source unit
+  const uint32_t vlat = (uint32_t)(lrow * lts2 + lunit * 16);
+  const int rrow = lane >> 3;                                    // row within the load
+  const int runit = (lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7);
+  const uint32_t vrope = (uint32_t)(rrow * rts2 + runit * 16);
+  // page ids of the item's first PT_MAX tiles in an LDS table (later tiles
+  // look theirs up in the page table)
+  int* const ptab = reinterpret_cast<int*>(ring + PTAB);
+  for (int tt = tid; tt < min(n_tiles, PT_MAX); tt += NW * 64)
+    ptab[tt] = pt_row[(t0 + tt * 64) >> p.page_shift];
+  // the query and page-id loads must be complete before the asm loads
+  // start counting, and the page-id table visible to every wave
   __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+  __syncthreads();
 
   const uint32_t ring_base = lds_u32(ring);
   const int64_t head_off = (int64_t)j * p.head_stride;
 
-  // this wave's share of the loads of tile t into stage u: load i covers
-  // latent rows (i * 1024 / LROW ...) or RoPE rows, lane -> (row, chunk)
+  // this wave's loads of tile t (clamped to the last tile) into stage u
   auto issue = [&](int t, int u) {
     const int tt = min(t, n_tiles - 1);
     const int key0 = t0 + tt * 64;                  // 64-aligned, inside one page
-    const int64_t page = sload_i32(pt_row + (key0 >> p.page_shift));
+    const int64_t page = tt < PT_MAX ? __builtin_amdgcn_readfirstlane(ptab[tt])
+                                     : sload_i32(pt_row + (key0 >> p.page_shift));
     const int slot0 = key0 & pmask;
-    // rows of this tile that exist: keys key0 .. t_last; later rows re-read
-    // row t_last (the trailing clamped issues re-read the last tile)
-    const int valid = max(1, min(64, t_end - key0));
-    const char* lbase =
-        p.pool0 + (page * p.page_stride + (int64_t)slot0 * p.token_stride + head_off) * 2;
-    const char* rbase = p.rope + (page * p.rpage_stride + (int64_t)slot0 * p.rtoken_stride) * 2;
+    const int valid = min(64, t_end - key0);        // rows of the tile that exist
+    const char* lbase = uniform_ptr(
+        p.pool0 + (page * p.page_stride + (int64_t)slot0 * p.token_stride + head_off) * 2);
+    const char* rbase =
+        uniform_ptr(p.rope + (page * p.rpage_stride + (int64_t)slot0 * p.rtoken_stride) * 2);
     const uint32_t sbase = ring_base + u * G::STAGE;
+    constexpr int LK = G::LLOADS / NW, RK = G::RLOADS / NW;
+    constexpr int RPB = G::PAIR ? 2 : 1;   // rows per latent block
+    if (valid == 64) {
 #pragma unroll
-    for (int k = 0; k < LPW; ++k) {
-      const int i = wave + k * NW;   // load index within the stage (wave-uniform)
-      if (i < G::LLOADS) {
-        constexpr int RPL = 1024 / G::LROW;          // latent rows per load
-        const int r = i * RPL + lane / G::LCPR;
-        const int c = (lane % G::LCPR) ^ (r & (G::LCPR - 1));
-        const int rr = min(r, valid - 1);
-        dma16(lbase + (int64_t)rr * p.token_stride * 2 + c * 16, sbase + i * 1024);
-      } else {
-        constexpr int RPLR = 1024 / G::RROW;
-        const int r = (i - G::LLOADS) * RPLR + lane / G::RCPR;
-        const int c = (lane % G::RCPR) ^ (r & (G::RCPR - 1));
-        const int rr = min(r, valid - 1);
-        dma16(rbase + (int64_t)rr * p.rtoken_stride * 2 + c * 16,
-              sbase + G::R_OFF + (i - G::LLOADS) * 1024);
+      for (int k = 0; k < LK; ++k) {
+        const int blk = wave + NW * k;
+        dma16(lbase + (int64_t)blk * RPB * lts2, vlat, sbase + blk * G::BSTR);
+      }
+#pragma unroll
+      for (int k = 0; k < RK; ++k) {
+        const int blk = wave + NW * k;
+        dma16(rbase + (int64_t)blk * 8 * rts2, vrope, sbase + G::R_OFF + blk * 1024);
+      }
+    } else {
+      // a partial last tile: rows past the end re-read the last row, so
+      // that stale cache contents never reach the MFMAs
+#pragma unroll
+      for (int k = 0; k < LK; ++k) {
+        const int blk = wave + NW * k;
+        const int r = min(blk * RPB + lrow, valid - 1);
+        dma16(lbase, (uint32_t)(r * lts2 + lunit * 16), sbase + blk * G::BSTR);
+      }
+#pragma unroll
+      for (int k = 0; k < RK; ++k) {
+        const int blk = wave + NW * k;
+        const int r = min(blk * 8 + rrow, valid - 1);
+        dma16(rbase, (uint32_t)(r * rts2 + runit * 16), sbase + G::R_OFF + blk * 1024);
       }
     }
   };
 
-  f32x4 acc[RT][NDVT];
+  // per-lane operand bases inside a stage (bytes).  K operand of key row
+  // r = 32 kh + 16 mt + col, unit 4 c + grp: 512-wide rows sit at r * BSTR;
+  // 256-wide row r in block r / 2, half r % 2, unit XOR-ed with 8 (r % 2),
+  // which moves unit 4 c + grp by +-8 units as bit 1 of c is clear / set
+  int s_lat_p, s_lat_m;
+  if constexpr (G::PAIR) {
+    const int bb = col & 1;
+    const int base = (16 * kh + (col >> 1)) * G::BSTR + bb * 512 + grp * 16;
+    s_lat_p = base + 128 * bb;
+    s_lat_m = base - 128 * bb;
+  } else {
+    s_lat_p = s_lat_m = (32 * kh + col) * G::BSTR + grp * 16;
+  }
+  // RoPE operand: row r as above, unit (4 c + grp) XOR (r / 2) mod 8, for
+  // the two RoPE k-chunks c = 0, 1
+  const int rx = (col >> 1) & 7;
+  const int s_rope0 = G::R_OFF + (32 * kh + col) * 128 + ((grp) ^ rx) * 16;
+  const int s_rope1 = G::R_OFF + (32 * kh + col) * 128 + ((4 + grp) ^ rx) * 16;
+  // V^T operand (transposing reads): rows 32 kc + 4 grp + col / 4 (+16),
+  // value units 2 d + (col % 4) / 2 with d = kh NDVH + dt, byte half col % 2
+  int v_tr_p, v_tr_m;
+  if constexpr (G::PAIR) {
+    const int bb = (col >> 2) & 1;
+    const int base = (2 * grp + (col >> 3)) * G::BSTR + bb * 512 + ((col & 3) >> 1) * 16 +
+                     (col & 1) * 8 + kh * G::NDVH * 32;
+    v_tr_p = base + 128 * bb;
+    v_tr_m = base - 128 * bb;
+  } else {
+    v_tr_p = v_tr_m = (4 * grp + (col >> 2)) * G::BSTR + ((col & 3) >> 1) * 16 + (col & 1) * 8 +
+                      kh * G::NDVH * 32;
+  }
+  // probability exchange: slot ((rh, kh), rt) of 1 KB, lane-linear
+  char* const pbuf = ring + PBUF;
+  const int p_wr = ((rh * 2 + kh) * RT) * 1024 + lane * 16;
+  const int p_rd = ((rh * 2) * RT) * 1024 + lane * 16;   // + (kc * RT + rt) * 1024
+  float* const tex = reinterpret_cast<float*>(pbuf);     // tile-max exchange (aliases pbuf)
+  const int t_wr = ((rh * 2 + kh) * RT) * 16 + col;
+  const int t_rd = ((rh * 2 + (kh ^ 1)) * RT) * 16 + col;
+
+  f32x4 acc[RT][G::NDVH];
   float m_ref[RT], l_run[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     m_ref[rt] = -INFINITY;
     l_run[rt] = 0.f;
 #pragma unroll
-    for (int i = 0; i < NDVT; ++i) acc[rt][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < G::NDVH; ++i) acc[rt][i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   bool over = false;
 
@@ -179,151 +266,211 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
 
   for (int t = 0; t < n_tiles; ++t) {
     const int u = t % STAGES;
-    issue(t + STAGES - 1, (t + STAGES - 1) % STAGES);
     {
-      constexpr int ahead = (STAGES - 1) * LPW;
+      constexpr int ahead = (STAGES - 2) * LPW;
       __builtin_amdgcn_s_waitcnt((ahead & 15) | ((ahead >> 4) << 14) | (0x7 << 4) | (0xf << 8));
     }
-    __syncthreads();  // every wave's loads of stage u have landed
+    // every wave's loads of tile t have landed, and every wave is done with
+    // tile t - 1 (its stage and the probability buffer are free again)
+    __syncthreads();
+    issue(t + STAGES - 1, (t + STAGES - 1) % STAGES);
     const char* sb = ring + u * G::STAGE;
     const int key0 = t0 + t * 64;
 
-    // scores S^T for the 64 keys: 4 M tiles of 16 keys, advanced together
-    // over the k-chunks (4 x RT independent MFMA accumulation chains)
-    f32x4 sa[RT][4];
+    // scores S^T for this wave's 32 keys: 2 M tiles x RT row tiles.  The K
+    // operand reads run KD steps ahead of the MFMAs that consume them
+    // (scheduling fences keep that order)
+    f32x4 sa[RT][2];
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+    for (int rt = 0; rt < RT; ++rt) sa[rt][0] = sa[rt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    {
+      constexpr int NS = 2 * G::NKC;   // step = (chunk c, M tile mt)
+      constexpr int KD = 6;
+      auto kread = [&](int st) {
+        const int c = st >> 1, mt = st & 1;
+        const char* src;
+        if (c < G::NKL)
+          src = sb + (((c >> 1) & 1) ? s_lat_m : s_lat_p) +
+                mt * (G::PAIR ? 8 : 16) * G::BSTR + c * 64;
+        else
+          src = sb + (c == G::NKL ? s_rope0 : s_rope1) + mt * 16 * 128;
+        return *reinterpret_cast<const bf16x8*>(src);
+      };
+      bf16x8 kb[KD];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) sa[rt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int st = 0; st < KD; ++st) kb[st] = kread(st);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int c = 0; c < NKC; ++c) {
-      const int ch = 4 * c + grp;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const int kr = mt * 16 + col;
-        const char* src = (ch < G::LCPR)
-            ? sb + kr * G::LROW + ((ch ^ (kr & (G::LCPR - 1))) * 16)
-            : sb + G::R_OFF + kr * G::RROW + (((ch - G::LCPR) ^ (kr & (G::RCPR - 1))) * 16);
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(src);
+      for (int st = 0; st < NS; ++st) {
+        const int c = st >> 1, mt = st & 1;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
-          sa[rt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[rt][c], sa[rt][mt], 0, 0, 0);
+          sa[rt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[st % KD], qreg[rt][c], sa[rt][mt],
+                                                               0, 0, 0);
+        if (st + KD < NS) kb[st % KD] = kread(st + KD);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      if (SB_K > 0 && (c % SB_K) == SB_K - 1) __builtin_amdgcn_sched_barrier(0);
     }
-    float s[RT][4][4];
+
+    // mask; lane holds keys key0 + 32 kh + 16 mt + 4 grp + i of row col
+    const bool full = (key0 + 64 <= t_end) && !p.causal;
+    float s[RT][2][4], tmax[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s[rt][mt][i] = sa[rt][mt][i] * p.scale_log2;
-
-    // mask + softmax
-    const bool full = (key0 + 64 <= t_end) && !p.causal;
-    bf16x8 pb[RT][2];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
+          float v = sa[rt][mt][i] * p.scale_log2;
           if (!full) {
-            const int key = key0 + mt * 16 + grp * 4 + i;
-            if (!(key < t_end && key <= qlimit[rt])) s[rt][mt][i] = -INFINITY;
+            const int key = key0 + 32 * kh + 16 * mt + 4 * grp + i;
+            if (!(key < t_end && key <= qlimit[rt])) v = -INFINITY;
           }
-          tmax = fmaxf(tmax, s[rt][mt][i]);
+          s[rt][mt][i] = v;
         }
-      tmax = wave_max4(tmax);
-      if constexpr (RESCALE) {
-        // raise the running max and rescale O and l
-        const float m_new = fmaxf(m_ref[rt], tmax);
-        const float m_u = (m_new == -INFINITY) ? 0.f : m_new;
-        const float a = __builtin_amdgcn_exp2f(m_ref[rt] - m_u);
-        l_run[rt] *= a;
+
+    // reference max shared by the pair (kh = 0, 1) of each row half: taken
+    // on the first tile (every tile when rescaling)
+    if (RESCALE || t == 0) {
 #pragma unroll
-        for (int dt = 0; dt < NDVT; ++dt) acc[rt][dt] *= a;
-        m_ref[rt] = m_new;
-      } else {
-        if (m_ref[rt] == -INFINITY) m_ref[rt] = tmax;
-        over |= tmax > m_ref[rt] + 64.f;
+      for (int rt = 0; rt < RT; ++rt) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[rt][mt][i]);
+        tmax[rt] = wave_max4(mx);
       }
+      if (grp == 0) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) tex[t_wr + rt * 16] = tmax[rt];
+      }
+      __syncthreads();
+      float other[RT];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) other[rt] = tex[t_rd + rt * 16];
+      __syncthreads();  // the exchange slots alias the probability buffer
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const float pair_max = fmaxf(tmax[rt], other[rt]);
+        if constexpr (RESCALE) {
+          const float m_new = fmaxf(m_ref[rt], pair_max);
+          const float a = __builtin_amdgcn_exp2f(m_ref[rt] - ((m_new == -INFINITY) ? 0.f : m_new));
+          l_run[rt] *= a;
+#pragma unroll
+          for (int dt = 0; dt < G::NDVH; ++dt) acc[rt][dt] *= a;
+          m_ref[rt] = m_new;
+        } else {
+          m_ref[rt] = pair_max;
+        }
+      }
+    }
+
+    bf16x8 pb[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
       const float m_use = (m_ref[rt] == -INFINITY) ? 0.f : m_ref[rt];
       float psum = 0.f;
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float e = __builtin_amdgcn_exp2f(s[rt][mt][i] - m_use);
+          const float x = s[rt][mt][i] - m_use;
+          // a score more than 2^64 above the reference (log2 units)
+          if constexpr (!RESCALE) over |= x > 64.f;
+          const float e = __builtin_amdgcn_exp2f(x);
           psum += e;
-          pb[rt][mt >> 1][(mt & 1) * 4 + i] = (__bf16)e;
+          pb[rt][mt * 4 + i] = (__bf16)e;
         }
       l_run[rt] += psum;
+      *reinterpret_cast<bf16x8*>(pbuf + p_wr + rt * 1024) = pb[rt];
     }
+    __syncthreads();  // both key halves' probabilities are in the buffer
 
-    // O^T += V^T P^T; per 32-key chunk kc the A operand holds keys
-    // 32 kc + 4 grp + e (e < 4) and 32 kc + 16 + 4 grp + (e - 4)
+    // O^T += V^T P^T over all 64 keys for this wave's value half; for the
+    // 32-key chunk kc the A operand holds keys 32 kc + 4 grp + e (e < 4)
+    // and 32 kc + 16 + 4 grp + (e - 4), matching the B operand written by
+    // wave kh = kc
+    {
+      bf16x8 pk[2][RT];
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-      const int kl0 = kc * 32 + grp * 4 + (col >> 2);
-      const int kl1 = kl0 + 16;
-#pragma unroll
-      for (int dt = 0; dt < NDVT; ++dt) {
-        const int cidx = 2 * dt + ((col & 3) >> 1);
-        const int half = (col & 1) * 8;
-        const char* s0 = sb + kl0 * G::LROW + ((cidx ^ (kl0 & (G::LCPR - 1))) * 16) + half;
-        const char* s1 = sb + kl1 * G::LROW + ((cidx ^ (kl1 & (G::LCPR - 1))) * 16) + half;
-        const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(s0));
-        const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(s1));
-        const bf16x8 va = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+      for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
-          acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[rt][kc], acc[rt][dt], 0, 0, 0);
-        if (SB_V > 0 && (dt % SB_V) == SB_V - 1) __builtin_amdgcn_sched_barrier(0);
+          pk[kc][rt] = *reinterpret_cast<const bf16x8*>(pbuf + p_rd + (kc * RT + rt) * 1024);
+      // step = (kc, dt); the two V^T reads of a step run VD steps ahead
+      constexpr int NP = 2 * G::NDVH;
+      constexpr int VD = 4;
+      auto vread = [&](int st) {
+        const int kc = st / G::NDVH, dt = st % G::NDVH;
+        constexpr int RS = G::PAIR ? 16 : 32;   // blocks per 32 keys
+        const char* s0 = sb + (((dt >> 2) & 1) ? v_tr_m : v_tr_p) + kc * RS * G::BSTR + dt * 32;
+        const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(s0));
+        const bf16x4 v1 =
+            __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(s0 + RS / 2 * G::BSTR));
+        return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+      };
+      bf16x8 vb[VD];
+#pragma unroll
+      for (int st = 0; st < VD; ++st) vb[st] = vread(st);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int st = 0; st < NP; ++st) {
+        const int kc = st / G::NDVH, dt = st % G::NDVH;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+          acc[rt][dt] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb[st % VD], pk[kc][rt], acc[rt][dt], 0, 0, 0);
+        if (st + VD < NP) vb[st % VD] = vread(st + VD);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    __syncthreads();  // every wave is done reading stage u
   }
-  __builtin_amdgcn_s_waitcnt(0);  // drain clamped trailing loads
+  __builtin_amdgcn_s_waitcnt(0);  // drain the clamped trailing loads
+  __syncthreads();                // the ring is free
 
-  if constexpr (!RESCALE) {
-    // workgroup-wide: did any row outgrow its reference?
-    if (tid == 0) *restart_flag = 0;
-    __syncthreads();
-    if (__builtin_amdgcn_ballot_w64(over) != 0 && lane == 0) *restart_flag = 1;
-    __syncthreads();
-    const bool again = *restart_flag != 0;
-    __syncthreads();
-    if (again) return true;
-  }
-
-  // ---- epilogue: lane holds O^T[dv = 16 dt + 4 grp + i][row]
+  // ---- workgroup-wide restart decision and the pair's row sums
+  int* const flag = reinterpret_cast<int*>(ring);
+  float* const lx = reinterpret_cast<float*>(ring + 256);
+  if (!RESCALE && lane == 0) flag[wave] = __builtin_amdgcn_ballot_w64(over) != 0 ? 1 : 0;
+  float lsum[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    const float l_row = wave_sum4(l_run[rt]);
+    lsum[rt] = wave_sum4(l_run[rt]);
+    if (grp == 0) lx[t_wr + rt * 16] = lsum[rt];
+  }
+  __syncthreads();
+  if constexpr (!RESCALE) {
+    if (flag[0] | flag[1] | flag[2] | flag[3]) return true;
+  }
+
+  // ---- epilogue: lane holds O^T[dv = DC/2 kh + 16 dt + 4 grp + i][row]
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const float l_row = lsum[rt] + lx[t_rd + rt * 16];
     const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
     const float lse_val =
         l_row > 0.f ? (m_ref[rt] + __log2f(l_row)) * 0.69314718055994531f : -INFINITY;
     if (!row_ok[rt]) continue;
     const int64_t orow = (int64_t)(b * p.q_len + tq[rt]) * p.h_q + hq[rt];
+    const int dv0 = kh * (DC / 2) + grp * 4;
     if (itm.n_splits <= 1) {
-      __bf16* o = reinterpret_cast<__bf16*>(p.out) + orow * DC;
+      __bf16* o = reinterpret_cast<__bf16*>(p.out) + orow * DC + dv0;
 #pragma unroll
-      for (int dt = 0; dt < NDVT; ++dt) {
+      for (int dt = 0; dt < G::NDVH; ++dt) {
         __bf16 v4[4] = {(__bf16)(acc[rt][dt][0] * inv), (__bf16)(acc[rt][dt][1] * inv),
                         (__bf16)(acc[rt][dt][2] * inv), (__bf16)(acc[rt][dt][3] * inv)};
-        *reinterpret_cast<uint2*>(o + dt * 16 + grp * 4) = __builtin_bit_cast(uint2, v4);
+        *reinterpret_cast<uint2*>(o + dt * 16) = __builtin_bit_cast(uint2, v4);
       }
-      if (p.lse && grp == 0) p.lse[orow] = lse_val;
+      if (p.lse && kh == 0 && grp == 0) p.lse[orow] = lse_val;
     } else {
       const int64_t prow =
           (int64_t)((itm.slot_base + itm.split) * p.q_len + tq[rt]) * p.h_q + hq[rt];
-      float* o = p.o_part + prow * DC;
+      float* o = p.o_part + prow * DC + dv0;
 #pragma unroll
-      for (int dt = 0; dt < NDVT; ++dt)
-        *reinterpret_cast<f32x4*>(o + dt * 16 + grp * 4) = acc[rt][dt] * inv;
-      if (grp == 0) p.lse_part[prow] = lse_val;
+      for (int dt = 0; dt < G::NDVH; ++dt)
+        *reinterpret_cast<f32x4*>(o + dt * 16) = acc[rt][dt] * inv;
+      if (kh == 0 && grp == 0) p.lse_part[prow] = lse_val;
     }
   }
   return false;
@@ -332,14 +479,13 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
 // RESCALE = false: the fixed-reference pass; records per workgroup whether
 // it had to give up (flags[block]).  RESCALE = true: the fix-up pass, a
 // second launch over the same grid that only works where the flag is set.
-template <int DC, int DR, int NW, int RT, int STAGES, bool RESCALE>
-__global__ __launch_bounds__(NW * 64) void decode_wide(Params p) {
+template <int DC, int DR, int RT, int STAGES, bool RESCALE>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void decode_wide(Params p) {
   using G = Geo<DC, DR>;
-  static_assert(G::LOADS % NW == 0, "loads split evenly over the waves");
-  static_assert(STAGES * G::STAGE <= 160 * 1024 - 1024, "LDS");
-  static_assert((STAGES - 1) * (G::LOADS / NW) <= 63, "vmcnt range");
-  __shared__ __attribute__((aligned(1024))) char ring[STAGES * G::STAGE];
-  __shared__ int restart_flag;
+  static_assert(STAGES * G::STAGE + 4 * RT * 1024 + PT_MAX * 4 <= 160 * 1024, "LDS");
+  static_assert((STAGES - 2) * (G::LOADS / NW) <= 63, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) char ring[STAGES * G::STAGE + 4 * RT * 1024 + PT_MAX * 4];
 
   if constexpr (RESCALE) {
     if (p.flags[blockIdx.x] == 0) return;
@@ -366,7 +512,7 @@ __global__ __launch_bounds__(NW * 64) void decode_wide(Params p) {
   itm.t_end = min(itm.t0 + chunk, itm.L);
   itm.n_tiles = (itm.t_end - itm.t0 + 63) / 64;
 
-  const bool gave_up = stream<DC, DR, NW, RT, STAGES, RESCALE>(p, itm, ring, &restart_flag);
+  const bool gave_up = stream<DC, DR, RT, STAGES, RESCALE>(p, itm, ring);
   if constexpr (!RESCALE) {
     if (threadIdx.x == 0) p.flags[blockIdx.x] = gave_up ? 1 : 0;
   }
@@ -374,34 +520,28 @@ __global__ __launch_bounds__(NW * 64) void decode_wide(Params p) {
 
 }  // namespace wide
 
-template <int DC, int DR, int NW, int RT, int S>
+template <int DC, int DR, int RT, int S>
 int launch_wide_one(Params p, int n_items, hipStream_t stream) {
   p.n_items = n_items;
-  p.row_blocks = (p.rows + 16 * NW * RT - 1) / (16 * NW * RT);
+  p.row_blocks = (p.rows + 32 * RT - 1) / (32 * RT);
   const int groups8 = (n_items + 7) / 8;
   const dim3 grid(groups8 * 8 * p.row_blocks);
-  hipLaunchKernelGGL((wide::decode_wide<DC, DR, NW, RT, S, false>), grid, dim3(NW * 64), 0,
+  hipLaunchKernelGGL((wide::decode_wide<DC, DR, RT, S, false>), grid, dim3(wide::NW * 64), 0,
                      stream, p);
   // fix-up pass: exits at once unless the first pass flagged the workgroup
-  hipLaunchKernelGGL((wide::decode_wide<DC, DR, NW, RT, S, true>), grid, dim3(NW * 64), 0,
+  hipLaunchKernelGGL((wide::decode_wide<DC, DR, RT, S, true>), grid, dim3(wide::NW * 64), 0,
                      stream, p);
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
-// Latent heads: two row tiles per wave; two or four waves by the group's rows;
-// as many 64-key stages as fit the LDS (2 for 512-wide, 3 for 256-wide).
+// Two row tiles per wave (64 rows per workgroup) unless the group has at
+// most 32 rows; as many 64-key stages as fit the LDS beside the probability
+// buffer (2 for 512-wide latents, 3 for 256-wide).
 template <int DC, int DR>
 int launch_wide(const Params& p, int n_items, hipStream_t stream) {
   constexpr int S = (DC >= 512) ? 2 : 3;
-  if constexpr (DC >= 512) {
-    // 512-wide latents: one row tile per wave keeps O (128 regs) and Q in
-    // the register file; 64 rows per workgroup
-    return launch_wide_one<DC, DR, 4, 1, S>(p, n_items, stream);
-  } else {
-    // every SIMD gets a wave: one row tile per wave up to 64 rows
-    if (p.rows <= 64) return launch_wide_one<DC, DR, 4, 1, S>(p, n_items, stream);
-    return launch_wide_one<DC, DR, 4, 2, S>(p, n_items, stream);
-  }
+  if (p.rows <= 32) return launch_wide_one<DC, DR, 1, S>(p, n_items, stream);
+  return launch_wide_one<DC, DR, 2, S>(p, n_items, stream);
 }
 
 }  // namespace
