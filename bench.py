@@ -155,6 +155,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--chunk-tokens", type=int, default=0, help="force the split chunk size")
+    ap.add_argument("--plan-mem", choices=["device", "host"], default="device",
+                    help="device: copy each step's plan to HBM; host: kernels read it from "
+                         "pinned host memory")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -213,25 +216,31 @@ def main():
     # still be in flight to the device), each [seqinfo rows | item rows], so a
     # step uploads its plan with one copy
     host_buf = [torch.zeros((B + max_items, 4), dtype=torch.int32).pin_memory() for _ in range(2)]
-    copied = [torch.cuda.Event(), torch.cuda.Event()]
+    # end event of the last step that read each host buffer
+    released = [None, None]
     dev_buf = torch.zeros((B + max_items, 4), dtype=torch.int32, device=dev)
 
     def make_plan(k):
         i = k % 2
-        copied[i].synchronize()
+        if released[i] is not None:
+            released[i].synchronize()
         hb = host_buf[i].numpy()
         st, plan = binding.attn_decode_plan(shp, seqlens_host, cu, args.chunk_tokens, hb[B:],
                                             hb[:B], max_items)
         if st != binding.ATTN_OK:
             raise binding.AttnError(st, "attn_decode_plan")
         n = B + plan.n_items
-        dev_buf[:n].copy_(host_buf[i][:n], non_blocking=True)
-        copied[i].record()
-        plan.seqinfo = dev_buf.data_ptr()
-        plan.items = dev_buf.data_ptr() + B * 16
-        return plan
+        if args.plan_mem == "host":
+            # pinned host memory is mapped into the device address space
+            base = host_buf[i].data_ptr()
+        else:
+            dev_buf[:n].copy_(host_buf[i][:n], non_blocking=True)
+            base = dev_buf.data_ptr()
+        plan.seqinfo = base
+        plan.items = base + B * 16
+        return plan, i
 
-    plan0 = make_plan(0)
+    plan0, _ = make_plan(0)
     torch.cuda.synchronize()
     ws_bytes = binding.attn_decode_workspace_size(plan0, H, d_v)
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
@@ -241,11 +250,14 @@ def main():
     stream = torch.cuda.current_stream(dev)
     s = stream.cuda_stream
 
-    def step(k, evs=None):
-        if evs is not None:
-            evs[0].record(stream)
-        plan = make_plan(k)
-        if evs is not None:
+    def step(k, evs, inner):
+        """One step: plan (host) + upload, decode, merge.  evs = [start,
+        before decode, after decode, end]; the inner two are recorded only
+        when `inner` (each recorded event costs the stream a few
+        microseconds, so steps without them give the step time)."""
+        evs[0].record(stream)
+        plan, slot = make_plan(k)
+        if inner:
             evs[1].record(stream)
         if w.kind == "gqa":
             st = binding.attn_decode_gqa(kv, q.data_ptr(), out.data_ptr(), lse.data_ptr(), T, H,
@@ -261,21 +273,24 @@ def main():
                                             plan, ws.data_ptr(), ws_bytes, s)
         if st != binding.ATTN_OK:
             raise binding.AttnError(st, "decode")
-        if evs is not None:
+        if inner:
             evs[2].record(stream)
         st = binding.attn_decode_merge(plan, H, d_v, kv.dtype, ws.data_ptr(), ws_bytes,
                                        out.data_ptr(), lse.data_ptr(), s)
         if st != binding.ATTN_OK:
             raise binding.AttnError(st, "merge")
-        if evs is not None:
-            evs[3].record(stream)
+        evs[3].record(stream)
+        released[slot] = evs[3]
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for k in range(args.warmup):
-        step(k)
+        step(k, [torch.cuda.Event() for _ in range(4)], False)
     torch.cuda.synchronize()
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # odd steps bracket the decode kernel for its launch duration; even
+    # steps (all steps when only one is timed) give the step time
+    inner = [args.steps > 1 and k % 2 == 1 for k in range(args.steps)]
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
@@ -284,13 +299,18 @@ def main():
             flush.fill_(k)
         elif args.flush == "read":
             flush.max()
-        step(k, evs[k])
+        step(k, evs[k], inner[k])
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
 
-    step_ms = np.array([e[0].elapsed_time(e[3]) for e in evs])
-    dec_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
-    merge_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
+    step_ms = np.array([e[0].elapsed_time(e[3]) for e, f in zip(evs, inner) if not f])
+    inst = [e for e, f in zip(evs, inner) if f] or evs[:0]
+    if inst:
+        dec_ms = np.array([e[1].elapsed_time(e[2]) for e in inst])
+        merge_ms = np.array([e[2].elapsed_time(e[3]) for e in inst])
+        inst_step_ms = np.array([e[0].elapsed_time(e[3]) for e in inst])
+    else:  # a single timed step: its whole time stands for the kernel
+        dec_ms = merge_ms = inst_step_ms = step_ms
     kvb = kv_bytes(w, seqlens_host)
     fl = flops(w, seqlens_host)
     ms = float(step_ms.mean())
@@ -322,12 +342,15 @@ def main():
                        "head_dim": w.head_dim, "d_rope": w.d_rope,
                        "mean_seqlen": float(seqlens_host.mean()), "page_size": w.page_size,
                        "kv_bytes_per_step": int(kvb), "gpus": 1, "layout": args.layout,
-                       "cache_flush": args.flush},
+                       "cache_flush": args.flush, "plan_mem": args.plan_mem},
             "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
             "tokens_per_s": round(tokens / (ms * 1e-3), 1),
             "step_ms_median": round(float(np.median(step_ms)), 5),
             "decode_ms_mean": round(float(dec_ms.mean()), 5),
             "merge_ms_mean": round(float(merge_ms.mean()), 5),
+            "instrumented_step_ms_mean": round(float(inst_step_ms.mean()), 5),
+            "timing": "value and ms_per_step from the steps without inner events; decode and "
+                      "merge times from the steps that bracket them",
             "wall_ms_per_step_incl_flush": round(1e3 * t_wall / args.steps, 5),
             "plan": {"items": int(plan0.n_items), "max_splits": int(plan0.max_splits),
                      "partial_slots": int(plan0.n_partial_slots)},

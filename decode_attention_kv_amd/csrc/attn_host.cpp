@@ -5,6 +5,7 @@
 #include "attn_kernels.h"
 
 #include <algorithm>
+#include <functional>
 #include <cstdint>
 #include <cstring>
 #include <vector>
@@ -15,30 +16,72 @@ using attn_internal::kTile;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Estimated cost, in bytes-equivalent, of the whole decode for chunks of
-// `ct` tiles: the larger of (total traffic spread over all CUs) and (the
-// longest single work item, which streams at only 1/W of a CU's bandwidth
-// when W workgroups share the CU), which bounds a greedy schedule's makespan.
-struct CostModel {
-  const std::vector<int64_t>* tiles;
-  int64_t groups, token_bytes, split_bytes, item_bytes, cu, wgs_per_cu;
-  double eval(int64_t ct) const {
-    int64_t total = 0, longest = 0;
-    bool any_split = false;
-    for (int64_t t : *tiles) {
-      int64_t n = std::max<int64_t>(1, ceil_div(t, ct));
-      int64_t kv = t * kTile * token_bytes;
-      total += groups * (kv + n * item_bytes + (n > 1 ? n * split_bytes : 0));
-      int64_t chunk = std::min<int64_t>(t, ct) * kTile * token_bytes;
-      longest = std::max(longest, chunk + item_bytes + (n > 1 ? split_bytes : 0));
-      any_split |= n > 1;
-    }
-    // the merge kernel is a second launch: about 2 microseconds of the
-    // whole GPU, i.e. what one CU streams in that time
-    const double merge = any_split ? 64.0 * 1024.0 : 0.0;
-    return std::max((double)total / (double)cu, (double)longest * (double)wgs_per_cu) + merge;
-  }
+// Items of a plan with chunks of `ct` tiles, in launch order: full chunks
+// first (all of equal length), then the shorter tails, longest first, so
+// that the dispatcher's in-order list scheduling ends with the short ones.
+// Each entry is (sequence, split, tiles); groups are expanded by the caller.
+struct Chunk {
+  int32_t b, s, tiles;
 };
+void chunks_in_order(const std::vector<int64_t>& tiles, int64_t ct, std::vector<Chunk>* out) {
+  out->clear();
+  std::vector<Chunk> tails;
+  const int batch = (int)tiles.size();
+  for (int b = 0; b < batch; ++b) {
+    const int64_t n = std::max<int64_t>(1, ceil_div(tiles[b], ct));
+    for (int64_t s = 0; s < n; ++s) {
+      const int64_t len = std::min<int64_t>(ct, tiles[b] - s * ct);
+      (len == ct ? *out : tails).push_back({b, (int32_t)s, (int32_t)len});
+    }
+  }
+  std::stable_sort(tails.begin(), tails.end(),
+                   [](const Chunk& x, const Chunk& y) { return x.tiles > y.tiles; });
+  out->insert(out->end(), tails.begin(), tails.end());
+}
+
+// Estimated decode time, in tiles at one workgroup's fair share, of the
+// plan with chunks of `ct` tiles: every XCD runs its workgroups (block i
+// goes to XCD i % 8) in launch order on `slots` slots; active workgroups
+// share the XCD's bandwidth, each at most `rmax` times its share at full
+// occupancy (processor sharing, simulated exactly with a virtual clock).
+double simulate(const std::vector<Chunk>& chunks, int groups, const attn_internal::KernelChoice& kc,
+                int slots) {
+  // Launch order of the kernels: item units (the groups of one chunk when
+  // `same_xcd_groups`, else single items with their row blocks) sit 8
+  // blocks apart, so XCD x receives units x, x + 8, x + 16, ... in order,
+  // each as `per_unit` consecutive workgroups.
+  const int64_t n_items = (int64_t)chunks.size() * groups;
+  const bool by_group = kc.same_xcd_groups;
+  const int64_t units = by_group ? (int64_t)chunks.size() : n_items;
+  const int per_unit = by_group ? groups : std::max(1, kc.row_blocks);
+  double makespan = 0.0;
+  std::vector<double> heap;
+  heap.reserve(slots);
+  for (int x = 0; x < 8; ++x) {
+    heap.clear();
+    double now = 0.0, vclock = 0.0;  // time, service each active workgroup got
+    auto retire_one = [&]() {
+      const double rate = std::min(kc.rmax, (double)slots / heap.size());
+      std::pop_heap(heap.begin(), heap.end(), std::greater<double>());
+      const double done = heap.back();
+      heap.pop_back();
+      now += (done - vclock) / rate;
+      vclock = done;
+    };
+    for (int64_t u = x; u < units; u += 8) {
+      const double work =
+          chunks[by_group ? u : u / groups].tiles + kc.fixed_tiles;
+      for (int k = 0; k < per_unit; ++k) {
+        if ((int)heap.size() == slots) retire_one();
+        heap.push_back(vclock + work);
+        std::push_heap(heap.begin(), heap.end(), std::greater<double>());
+      }
+    }
+    while (!heap.empty()) retire_one();
+    makespan = std::max(makespan, now);
+  }
+  return makespan;
+}
 
 }  // namespace
 
@@ -93,43 +136,70 @@ int attn_decode_plan(const attn_shape_t* shape, const int32_t* seqlens_host, int
   }
 
   int64_t ct;  // chunk length in tiles
+  std::vector<Chunk> chunks;
+  chunks.reserve(1024);
   if (chunk_tokens > 0) {
     ct = chunk_tokens / kTile;
   } else {
+    // Pick the chunk length minimising simulated decode time plus the merge
+    // of split partials.  Times in microseconds: a tile at a workgroup's
+    // fair share of about 6 TB/s; the merge launch costs about 4 us, plus
+    // about 0.55 us per split of the longest sequence, plus the partials'
+    // write and re-read at about 5 TB/s.
+    const int slots = std::max(1, cu_count / 8) * kc.wgs_per_cu;  // per XCD
+    const double tile_us =
+        (double)kTile * token_bytes / (6.0e6 / ((double)cu_count * kc.wgs_per_cu));
     const int64_t rows = (int64_t)(h_q / n_groups) * q_len;
-    CostModel m;
-    m.tiles = &tiles;
-    m.groups = n_groups;
-    m.token_bytes = token_bytes;
-    // a split writes and the merge re-reads fp32 O and LSE for its rows
-    m.split_bytes = 2 * rows * (d_v + 1) * 4;
-    // fixed cost of an item: its query rows plus prologue/epilogue latency,
-    // taken as the bytes one CU streams in about 1.5 microseconds
-    m.item_bytes = rows * (d_v + 64) * 2 + 48 * 1024;
-    m.cu = cu_count;
-    m.wgs_per_cu = kc.wgs_per_cu;
-    ct = max_tiles;
-    double best = m.eval(ct);
-    // candidate chunk lengths: the shortest chunk giving the longest sequence
-    // n splits, for every n (about 2 sqrt(max_tiles) distinct values)
-    int64_t prev = max_tiles;
-    for (int64_t n = 2; n <= max_tiles; ++n) {
+    // cost of splitting the longest sequence n ways (microseconds)
+    auto cost = [&](int n, int64_t* c_out) -> double {
       const int64_t c = ceil_div(max_tiles, n);
-      if (c == prev) continue;
-      prev = c;
-      const double v = m.eval(c);
-      if (v < best * 0.999) { best = v; ct = c; }
+      *c_out = c;
+      if (c < std::min<int64_t>(4, max_tiles)) return -1.0;  // chunks of >= 256 keys
+      chunks_in_order(tiles, c, &chunks);
+      const int64_t wgs = (int64_t)chunks.size() * n_groups;
+      if (wgs > max_items || wgs > 6 * 8 * (int64_t)slots) return -1.0;
+      double t = simulate(chunks, n_groups, kc, slots) * tile_us;
+      int64_t slots_used = 0, splits = 1;
+      for (int b = 0; b < batch; ++b) {
+        const int64_t nb = std::max<int64_t>(1, ceil_div(tiles[b], c));
+        if (nb > 1) slots_used += nb;
+        splits = std::max(splits, nb);
+      }
+      if (slots_used > 0)
+        t += 4.0 + 0.55 * splits + 2.0 * slots_used * n_groups * rows * (d_v + 1) * 4 / 5.0e6;
+      return t;
+    };
+    // coarse pass over powers of two, then the neighbours of the best
+    double best = 0.0;
+    int best_n = 1;
+    ct = max_tiles;
+    auto consider = [&](int n) {
+      int64_t c;
+      const double t = cost(n, &c);
+      if (t >= 0.0 && (best_n == 0 || t < best * 0.995)) {
+        best = t;
+        best_n = n;
+        ct = c;
+      }
+    };
+    best_n = 0;
+    for (int n = 1; n <= 64; n *= 2) {
+      consider(n);
+      if (best_n > 0 && n >= 4 * best_n) break;  // two steps past the best
     }
+    const int n0 = best_n;
+    if (n0 > 1) consider(n0 * 3 / 4);
+    consider(n0 * 3 / 2);
+    if (best_n == 0) ct = max_tiles;
   }
+  chunks_in_order(tiles, ct, &chunks);
 
-  // items: full-length chunks first (longest-first), then the shorter tails
-  int64_t n_items = 0, slot = 0;
+  // items in launch order, groups of one chunk consecutive
+  const int64_t n_items = (int64_t)chunks.size() * n_groups;
+  int64_t slot = 0;
   int max_splits = 1;
-  for (int b = 0; b < batch; ++b) {
-    int64_t n = std::max<int64_t>(1, ceil_div(tiles[b], ct));
-    n_items += n * n_groups;
-    max_splits = (int)std::max<int64_t>(max_splits, n);
-  }
+  for (int b = 0; b < batch; ++b)
+    max_splits = (int)std::max<int64_t>(max_splits, std::max<int64_t>(1, ceil_div(tiles[b], ct)));
   if (n_items > max_items) return ATTN_ERR_WORKSPACE;
 
   const int32_t chunk = (int32_t)(ct * kTile);
@@ -142,22 +212,13 @@ int attn_decode_plan(const attn_shape_t* shape, const int32_t* seqlens_host, int
     if (n > 1) slot += n;
   }
   int64_t k = 0;
-  for (int pass = 0; pass < 2; ++pass) {
-    for (int b = 0; b < batch; ++b) {
-      const int64_t L = seqlens_host[b];
-      const int64_t n = seqinfo_host[4 * b + 0];
-      for (int64_t s = 0; s < n; ++s) {
-        const int64_t t0 = s * chunk;
-        const bool full = (t0 + chunk) <= L;
-        if ((pass == 0) != full) continue;
-        for (int j = 0; j < n_groups; ++j) {
-          items_host[4 * k + 0] = b;
-          items_host[4 * k + 1] = j;
-          items_host[4 * k + 2] = (int32_t)s;
-          items_host[4 * k + 3] = (int32_t)t0;
-          ++k;
-        }
-      }
+  for (const Chunk& c : chunks) {
+    for (int j = 0; j < n_groups; ++j) {
+      items_host[4 * k + 0] = c.b;
+      items_host[4 * k + 1] = j;
+      items_host[4 * k + 2] = c.s;
+      items_host[4 * k + 3] = (int32_t)((int64_t)c.s * chunk);
+      ++k;
     }
   }
   plan->n_items = (int32_t)n_items;

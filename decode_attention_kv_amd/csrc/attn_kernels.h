@@ -22,6 +22,16 @@ struct KernelChoice {
   int64_t token_bytes; // cache bytes one work item reads per token
   int rows;            // query rows per group: (h_q / groups) * q_len
   int d_v;             // output width per head
+  // Dispatch model used by the planner (fitted to measured chunk sweeps on
+  // MI355X): workgroups are dealt to the 8 XCDs by block index; the groups
+  // of one (sequence, chunk) go to one XCD when `same_xcd_groups`, and the
+  // `row_blocks` workgroups of one item always do.  Active workgroups of an
+  // XCD share its bandwidth; one alone runs at most `rmax` times its share
+  // at full occupancy; every workgroup costs `fixed_tiles` extra tiles.
+  bool same_xcd_groups;
+  int row_blocks;
+  double rmax;
+  double fixed_tiles;
 };
 
 // Bytes of one 64-key stage of the streaming kernel (four waves x 16 keys).
@@ -68,9 +78,14 @@ inline KernelChoice choose_kernel(const attn_shape_t& sh) {
                     (sh.head_dim == 512 || sh.head_dim == 256);
   if (env_force_general()) narrow = false;
   k.narrow = narrow || (wide && !env_force_general());
+  k.same_xcd_groups = false;
+  k.row_blocks = 1;
   if (k.narrow && sh.kind == ATTN_KIND_LATENT) {
     k.stages = sh.head_dim >= 512 ? 2 : 3;
     k.wgs_per_cu = 1;
+    k.row_blocks = k.rows <= 32 ? 1 : (k.rows + 63) / 64;
+    k.rmax = 1.1;
+    k.fixed_tiles = 6.0;
     return k;
   }
   if (narrow) {
@@ -78,9 +93,18 @@ inline KernelChoice choose_kernel(const attn_shape_t& sh) {
     const int lds = k.stages * narrow_stage_bytes(sh.kind, sh.head_dim, sh.d_rope) + 2048;
     int w = 163840 / lds;
     k.wgs_per_cu = w < 1 ? 1 : w > 2 ? 2 : w;
+    // GTA groups read the same RoPE key rows: keep them on one XCD's L2
+    k.same_xcd_groups = sh.kind == ATTN_KIND_GTA;
+    k.rmax = sh.kind == ATTN_KIND_GTA ? 1.5 : 3.0;
+    k.fixed_tiles = sh.kind == ATTN_KIND_GTA ? 3.0 : 2.0;
   } else {
     k.stages = 1;
     k.wgs_per_cu = 1;
+    // general kernel: 64 rows per workgroup for 512-wide latents, else 128
+    const int rows_per_wg = (sh.kind == ATTN_KIND_LATENT && sh.head_dim >= 512) ? 64 : 128;
+    k.row_blocks = (k.rows + rows_per_wg - 1) / rows_per_wg;
+    k.rmax = 1.5;
+    k.fixed_tiles = 2.0;
   }
   return k;
 }

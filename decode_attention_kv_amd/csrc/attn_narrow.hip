@@ -217,10 +217,10 @@ __global__ __launch_bounds__(NW * 64) void decode_narrow(Params p) {
   const int grp = lane >> 4;
 
   // Workgroups are dealt round-robin to the 8 XCDs (block i -> XCD i % 8).
-  // The plan lists the groups of one (sequence, chunk) consecutively; they
-  // are mapped to blocks 8 apart so they share one XCD's L2 (GTA's RoPE key
-  // rows are read by every group).
-  const int gsz = p.row_blocks;  // groups per (sequence, chunk)
+  // The plan lists the groups of one (sequence, chunk) consecutively; with
+  // gsz > 1 they are mapped to blocks 8 apart so they share one XCD's L2
+  // (GTA's RoPE key rows are read by every group); gsz = 1 keeps plan order.
+  const int gsz = p.row_blocks;  // items per unit kept on one XCD
   const int bid = blockIdx.x;
   const int blk = bid / (8 * gsz);
   const int rem = bid - blk * 8 * gsz;
@@ -593,8 +593,12 @@ int launch_narrow_s(Params p, int n_items, int groups, hipStream_t stream) {
     return launch_narrow_s<KIND, D, DR, RT, S - 1>(p, n_items, groups, stream);
   } else {
     p.n_items = n_items;
-    p.row_blocks = groups;
-    const int blocks = (n_items + 8 * groups - 1) / (8 * groups) * 8 * groups;
+    // GTA: the groups of one (sequence, chunk) share an XCD (its L2 serves
+    // their common RoPE key rows); GQA groups share nothing and are dealt
+    // round-robin like any item, which balances the XCDs
+    const int gsz = KIND == GTA ? groups : 1;
+    p.row_blocks = gsz;
+    const int blocks = (n_items + 8 * gsz - 1) / (8 * gsz) * 8 * gsz;
     hipLaunchKernelGGL((narrow::decode_narrow<KIND, D, DR, RT, S>), dim3(blocks),
                        dim3(narrow::NW * 64), 0, stream, p);
     return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
