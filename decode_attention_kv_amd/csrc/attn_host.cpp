@@ -152,12 +152,14 @@ int attn_decode_plan(const attn_shape_t* shape, const int32_t* seqlens_host, int
     const int64_t rows = (int64_t)(h_q / n_groups) * q_len;
     // cost of splitting the longest sequence n ways (microseconds)
     auto cost = [&](int n, int64_t* c_out) -> double {
+      if (n < 1) return -1.0;
       const int64_t c = ceil_div(max_tiles, n);
       *c_out = c;
       if (c < std::min<int64_t>(4, max_tiles)) return -1.0;  // chunks of >= 256 keys
       chunks_in_order(tiles, c, &chunks);
       const int64_t wgs = (int64_t)chunks.size() * n_groups;
-      if (wgs > max_items || wgs > 6 * 8 * (int64_t)slots) return -1.0;
+      if (wgs > max_items) return -1.0;
+      if (n > 1 && wgs > 6 * 8 * (int64_t)slots) return -1.0;  // far finer than the GPU
       double t = simulate(chunks, n_groups, kc, slots) * tile_us;
       int64_t slots_used = 0, splits = 1;
       for (int b = 0; b < batch; ++b) {
@@ -189,7 +191,7 @@ int attn_decode_plan(const attn_shape_t* shape, const int32_t* seqlens_host, int
     }
     const int n0 = best_n;
     if (n0 > 1) consider(n0 * 3 / 4);
-    consider(n0 * 3 / 2);
+    if (n0 > 0) consider(n0 * 3 / 2);
     if (best_n == 0) ct = max_tiles;
   }
   chunks_in_order(tiles, ct, &chunks);

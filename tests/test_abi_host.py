@@ -87,8 +87,24 @@ def test_plan_is_deterministic_and_longest_first():
     items, info = a[2], a[3]
     lens = [min(t0 + info[b_, 3], info[b_, 2]) - t0 for b_, _, _, t0 in items.tolist()]
     full = [l == info[b_, 3] for (b_, _, _, _), l in zip(items.tolist(), lens)]
-    # all full-length chunks come before any shorter tail chunk
+    # all full-length chunks come before any shorter tail chunk, and the
+    # tails follow longest first
     assert full == sorted(full, reverse=True)
+    tails = [l for l, f in zip(lens, full) if not f]
+    assert tails == sorted(tails, reverse=True)
+
+
+@pytest.mark.parametrize("batch,groups,kind", [(512, 8, "gqa"), (4096, 8, "gqa"),
+                                               (256, 1, "latent")])
+def test_plan_large_batches(batch, groups, kind):
+    # many more work items than the GPU has slots, with ragged lengths
+    rng = np.random.default_rng(batch)
+    seqlens = rng.integers(1, 20000, size=batch).astype(np.int32)
+    d, d_rope, h_q = (128, 0, 32) if kind == "gqa" else (512, 64, 128)
+    st, plan, items, info = _plan(seqlens, h_q=h_q, groups=groups, kind=kind, d=d,
+                                  d_rope=d_rope)
+    assert st == 0 and plan.n_items == len(items) >= batch * groups
+    assert info[:, 3].min() == info[:, 3].max() and info[0, 3] % 64 == 0
 
 
 def test_plan_auto_split_balances_load():
