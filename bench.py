@@ -219,6 +219,7 @@ def main():
     # end event of the last step that read each host buffer
     released = [None, None]
     dev_buf = torch.zeros((B + max_items, 4), dtype=torch.int32, device=dev)
+    counters = None  # merge counters (zero-filled once), sized from the first plan
 
     def make_plan(k):
         i = k % 2
@@ -238,6 +239,11 @@ def main():
             base = dev_buf.data_ptr()
         plan.seqinfo = base
         plan.items = base + B * 16
+        nonlocal counters
+        if counters is None:
+            counters = torch.zeros(max(1, binding.attn_decode_counter_count(plan, H)),
+                                   dtype=torch.int32, device=dev)
+        plan.counters = counters.data_ptr()
         return plan, i
 
     plan0, _ = make_plan(0)

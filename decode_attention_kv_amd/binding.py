@@ -55,7 +55,7 @@ def shape(kind: str, dtype: int, batch: int, q_len: int, h_q: int, groups: int, 
 class Plan(Structure):
     _fields_ = [("n_items", c_int32), ("batch", c_int32), ("n_groups", c_int32),
                 ("q_len", c_int32), ("max_splits", c_int32), ("n_partial_slots", c_int32),
-                ("items", c_void_p), ("seqinfo", c_void_p)]
+                ("items", c_void_p), ("seqinfo", c_void_p), ("counters", c_void_p)]
 
 
 class AttnError(RuntimeError):
@@ -84,6 +84,8 @@ def lib():
     L.attn_decode_plan.restype = c_int
     L.attn_decode_workspace_size.argtypes = [POINTER(Plan), c_int, c_int]
     L.attn_decode_workspace_size.restype = c_size_t
+    L.attn_decode_counter_count.argtypes = [POINTER(Plan), c_int]
+    L.attn_decode_counter_count.restype = c_size_t
     common_tail = [c_float, c_int, POINTER(Plan), c_void_p, c_size_t, c_void_p]
     L.attn_decode_gqa.argtypes = ([POINTER(PagedKV), c_void_p, c_void_p, c_void_p, c_int, c_int,
                                    c_int, c_int] + common_tail)
@@ -126,6 +128,10 @@ def attn_decode_plan(shape_: Shape, seqlens_host: np.ndarray, cu_count: int, chu
 
 def attn_decode_workspace_size(plan: Plan, h_q: int, d_v: int) -> int:
     return lib().attn_decode_workspace_size(ctypes.byref(plan), h_q, d_v)
+
+
+def attn_decode_counter_count(plan: Plan, h_q: int) -> int:
+    return lib().attn_decode_counter_count(ctypes.byref(plan), h_q)
 
 
 def attn_decode_gqa(kv, q, out, lse, q_len, h_q, h_kv, d, scale, flags, plan, ws, ws_bytes,
@@ -192,7 +198,8 @@ def paged_kv(pool0, pool1, rope, page_table, seqlens) -> PagedKV:
 class DevicePlan:
     """A host plan plus its device copy (keeps the device arrays alive)."""
 
-    def __init__(self, shape_: Shape, seqlens_host, device, cu_count=256, chunk_tokens=0):
+    def __init__(self, shape_: Shape, seqlens_host, device, cu_count=256, chunk_tokens=0,
+                 fused_merge=True):
         import torch
 
         seqlens_host = np.ascontiguousarray(seqlens_host, dtype=np.int32)
@@ -211,19 +218,27 @@ class DevicePlan:
         self.seqinfo_dev = torch.from_numpy(self.seqinfo_host).to(device)
         plan.items = self.items_dev.data_ptr()
         plan.seqinfo = self.seqinfo_dev.data_ptr()
+        # merge counters, zero-filled once; with them the streaming kernels
+        # merge split rows themselves
+        self.counters = None
+        if fused_merge:
+            n = attn_decode_counter_count(plan, shape_.h_q)
+            self.counters = torch.zeros(max(n, 1), dtype=torch.int32, device=device)
+            plan.counters = self.counters.data_ptr()
         self.plan = plan
 
 
 def decode(kind: str, q, pool0, pool1, rope, page_table, seqlens, seqlens_host, *, groups: int,
            scale: float, causal: bool = False, rope_theta: float = 0.0, d_rope: int = 0,
            out=None, lse=None, chunk_tokens: int = 0, cu_count: int = 256, plan=None,
-           workspace=None, stream=None, defer_merge: bool = False):
+           workspace=None, stream=None, defer_merge: bool = False, fused_merge: bool = True):
     """Run one decode through the native library on torch tensors.
 
     kind: "gqa" | "gta" | "latent".  q [B, T, H, Dq]; pools as in the header.
     Returns (out, lse, plan, workspace) so callers can reuse plan/workspace.
     With ``defer_merge`` the split partials stay in the workspace and the
-    caller finishes with ``merge``.
+    caller finishes with ``merge``.  A new plan carries merge counters unless
+    ``fused_merge`` is false (then the merge is a second launch).
     """
     import torch
 
@@ -233,7 +248,8 @@ def decode(kind: str, q, pool0, pool1, rope, page_table, seqlens, seqlens_host, 
     if plan is None:
         dtype = ATTN_BF16 if pool0.dtype == torch.bfloat16 else ATTN_FP32
         sh = shape(kind, dtype, B, T, H, groups, width, d_rope, pool0.shape[1], causal)
-        plan = DevicePlan(sh, seqlens_host, q.device, cu_count=cu_count, chunk_tokens=chunk_tokens)
+        plan = DevicePlan(sh, seqlens_host, q.device, cu_count=cu_count, chunk_tokens=chunk_tokens,
+                          fused_merge=fused_merge)
     need = attn_decode_workspace_size(plan.plan, H, d_v)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)

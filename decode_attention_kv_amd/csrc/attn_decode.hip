@@ -116,6 +116,7 @@ void set_partials(Params& p, const attn_plan_t* plan, const void* ws, int q_len,
     p.lse_part = reinterpret_cast<float*>(w + (rows * d_v * 4 + 255) / 256 * 256);
   }
   p.flags = reinterpret_cast<int32_t*>(w + attn_internal::flags_offset(plan, h_q, d_v));
+  p.counters = plan->counters;
 }
 
 void fill_common(Params& p, const attn_paged_kv_t* kv, const void* q, void* out, float* lse,
@@ -214,8 +215,11 @@ int attn_decode_gqa(const attn_paged_kv_t* kv, const void* q, void* out, float* 
   const attn_internal::KernelChoice kc =
       choice_for(kv, ATTN_KIND_GQA, q_len, h_q, h_kv, d, 0, flags);
   if (kc.narrow) {
+    // the streaming kernel merges split rows itself when the plan carries
+    // counters (and the merge is not deferred); otherwise a merge launch
+    p.fuse_merge = (!(flags & ATTN_DEFER_MERGE) && plan->counters) ? 1 : 0;
     st = run_narrow(GQA, d, p, plan->n_items, h_kv, kc.stages, stream);
-    if (st != ATTN_OK || (flags & ATTN_DEFER_MERGE)) return st;
+    if (st != ATTN_OK || (flags & ATTN_DEFER_MERGE) || p.fuse_merge) return st;
     return d == 128 ? launch_combine<__bf16, 128>(p, plan, stream)
                     : launch_combine<__bf16, 64>(p, plan, stream);
   }
@@ -238,8 +242,9 @@ int attn_decode_gta(const attn_paged_kv_t* kv, const void* q, void* out, float* 
   const attn_internal::KernelChoice kc =
       choice_for(kv, ATTN_KIND_GTA, q_len, h_q, h_kv, d, d_rope, flags);
   if (kc.narrow) {
+    p.fuse_merge = (!(flags & ATTN_DEFER_MERGE) && plan->counters) ? 1 : 0;
     st = run_narrow(GTA, d, p, plan->n_items, h_kv, kc.stages, stream);
-    if (st != ATTN_OK || (flags & ATTN_DEFER_MERGE)) return st;
+    if (st != ATTN_OK || (flags & ATTN_DEFER_MERGE) || p.fuse_merge) return st;
     return launch_combine<__bf16, 128>(p, plan, stream);
   }
   return run<GTA, __bf16, 128, 64>(p, plan, flags, stream);
@@ -261,8 +266,9 @@ int attn_decode_latent(const attn_paged_kv_t* kv, const void* q, void* out, floa
   const bool offsets_fit = 64 * 2 * kv->token_stride < (1LL << 31) &&
                            64 * 2 * kv->rope_token_stride < (1LL << 31);
   if (kc.narrow && offsets_fit) {
+    p.fuse_merge = (!(flags & ATTN_DEFER_MERGE) && plan->counters) ? 1 : 0;
     st = run_wide(d_c, p, plan->n_items, stream);
-    if (st != ATTN_OK || (flags & ATTN_DEFER_MERGE)) return st;
+    if (st != ATTN_OK || (flags & ATTN_DEFER_MERGE) || p.fuse_merge) return st;
     return d_c == 512 ? launch_combine<__bf16, 512>(p, plan, stream)
                       : launch_combine<__bf16, 256>(p, plan, stream);
   }

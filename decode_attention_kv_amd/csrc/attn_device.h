@@ -41,6 +41,8 @@ struct Params {
   float* o_part;
   float* lse_part;
   int32_t* flags;     // latent streaming kernel: per-workgroup fix-up flags
+  uint32_t* counters; // merge arrival counters (streaming kernels)
+  int32_t fuse_merge; // streaming kernels: the last split workgroup merges
   const int32_t* items;
   const int32_t* seqinfo;
   int32_t q_len, h_q, g, rows;  // rows = g * q_len per group
@@ -94,6 +96,59 @@ __device__ __forceinline__ int sload_i32(const int32_t* ptr) {
   int v;
   asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(up));
   return v;
+}
+
+// Merge of split partials (Hydragen's softmax-denominator decomposition on
+// the "Efficient Inference" tag page) for rows [row0, row0 + nrows) of group
+// j of sequence b: M = max_s lse_s, w_s = exp(lse_s - M),
+// out = sum_s w_s O_s / sum_s w_s, lse = M + ln sum_s w_s.  Every thread of
+// the workgroup takes (row, 4 columns) units.
+template <int DV>
+__device__ __forceinline__ void merge_split_rows(const Params& p, int b, int j, int row0, int nrows,
+                                                 int n_splits, int slot_base) {
+  constexpr int C4 = DV / 4;
+  for (int w = threadIdx.x; w < nrows * C4; w += blockDim.x) {
+    const int r = row0 + w / C4;
+    const int c4 = (w % C4) * 4;
+    const int tq = r / p.g;
+    const int hq = j * p.g + (r - tq * p.g);
+    float M = -INFINITY;
+    for (int s = 0; s < n_splits; ++s)
+      M = fmaxf(M, p.lse_part[((int64_t)(slot_base + s) * p.q_len + tq) * p.h_q + hq]);
+    const float Ms = (M == -INFINITY) ? 0.f : M;
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+    float W = 0.f;
+    for (int s = 0; s < n_splits; ++s) {
+      const int64_t pr = ((int64_t)(slot_base + s) * p.q_len + tq) * p.h_q + hq;
+      const float wt = __expf(p.lse_part[pr] - Ms);
+      W += wt;
+      a += wt * *reinterpret_cast<const f32x4*>(p.o_part + pr * DV + c4);
+    }
+    const float inv = W > 0.f ? 1.f / W : 0.f;
+    const int64_t orow = ((int64_t)b * p.q_len + tq) * p.h_q + hq;
+    __bf16 v4[4] = {(__bf16)(a[0] * inv), (__bf16)(a[1] * inv), (__bf16)(a[2] * inv),
+                    (__bf16)(a[3] * inv)};
+    *reinterpret_cast<uint2*>(reinterpret_cast<__bf16*>(p.out) + orow * DV + c4) =
+        __builtin_bit_cast(uint2, v4);
+    if (p.lse && c4 == 0) p.lse[orow] = W > 0.f ? Ms + __logf(W) : -INFINITY;
+  }
+}
+
+// After this workgroup wrote its split's partials: count its arrival on
+// `counter`; the last of the n_splits arrivals (atomicInc wraps the counter
+// to zero) merges the rows.  `is_last` is a workgroup-shared int.
+template <int DV>
+__device__ __forceinline__ void arrive_and_merge(const Params& p, uint32_t* counter, int* is_last,
+                                                 int b, int j, int row0, int nrows, int n_splits,
+                                                 int slot_base) {
+  __threadfence();  // this workgroup's partials are visible device-wide
+  __syncthreads();
+  if (threadIdx.x == 0) *is_last = atomicInc(counter, (unsigned)(n_splits - 1)) == (unsigned)(n_splits - 1);
+  __syncthreads();
+  if (*is_last) {
+    __threadfence();  // and so are every other split's
+    merge_split_rows<DV>(p, b, j, row0, nrows, n_splits, slot_base);
+  }
 }
 
 // Launchers, one per kernel family (each in its own translation unit).

@@ -231,7 +231,15 @@ int attn_decode_plan(const attn_shape_t* shape, const int32_t* seqlens_host, int
   plan->n_partial_slots = (int32_t)slot;
   plan->items = nullptr;
   plan->seqinfo = nullptr;
+  plan->counters = nullptr;
   return ATTN_OK;
+}
+
+size_t attn_decode_counter_count(const attn_plan_t* plan, int h_q) {
+  if (!plan || h_q <= 0 || plan->batch <= 0 || plan->n_groups <= 0 || plan->q_len <= 0 ||
+      h_q % plan->n_groups)
+    return 0;
+  return attn_internal::counter_count(plan, h_q);
 }
 
 size_t attn_decode_workspace_size(const attn_plan_t* plan, int h_q, int d_v) {

@@ -117,10 +117,18 @@ inline size_t flags_offset(const attn_plan_t* plan, int h_q, int d_v) {
   const size_t rows = (size_t)plan->n_partial_slots * plan->q_len * h_q;
   return (rows * d_v * 4 + 255) / 256 * 256 + (rows * 4 + 255) / 256 * 256;
 }
-inline size_t flags_bytes(const attn_plan_t* plan, int h_q) {
+inline int64_t row_blocks_of(const attn_plan_t* plan, int h_q) {
   const int64_t rows = (int64_t)(plan->n_groups > 0 ? h_q / plan->n_groups : 0) * plan->q_len;
-  const int64_t blocks = (plan->n_items + 7) / 8 * 8 * ((rows + 63) / 64 > 0 ? (rows + 63) / 64 : 1);
-  return (size_t)blocks * 4;
+  return (rows + 63) / 64 > 0 ? (rows + 63) / 64 : 1;
+}
+inline size_t flags_bytes(const attn_plan_t* plan, int h_q) {
+  const int64_t blocks = (plan->n_items + 7) / 8 * 8 * row_blocks_of(plan, h_q);
+  return ((size_t)blocks * 4 + 255) / 256 * 256;
+}
+// Merge arrival counters (plan->counters): one per (sequence, group, block
+// of 64 rows), indexed (b * groups + j) * row_blocks + block.
+inline size_t counter_count(const attn_plan_t* plan, int h_q) {
+  return (size_t)plan->batch * plan->n_groups * row_blocks_of(plan, h_q);
 }
 
 }  // namespace attn_internal

@@ -209,6 +209,7 @@ __global__ __launch_bounds__(NW * 64) void decode_narrow(Params p) {
   __shared__ __attribute__((aligned(1024))) char st4[STAGES > 4 ? G::STAGE_BYTES : 16];
   __shared__ __attribute__((aligned(1024))) char st5[STAGES > 5 ? G::STAGE_BYTES : 16];
   __shared__ float merge_m[NW][16 * RT], merge_l[NW][16 * RT];
+  __shared__ int merge_last;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -582,6 +583,10 @@ __global__ __launch_bounds__(NW * 64) void decode_narrow(Params p) {
       }
     }
   }
+  // the last split of this (sequence, group) to finish merges all splits
+  if (n_splits > 1 && p.fuse_merge)
+    arrive_and_merge<D>(p, p.counters + (int64_t)b * (p.h_q / p.g) + j, &merge_last, b, j, 0,
+                        p.rows, n_splits, slot_base);
 }
 
 }  // namespace narrow

@@ -473,6 +473,14 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
       if (kh == 0 && grp == 0) p.lse_part[prow] = lse_val;
     }
   }
+  // the last split of this (sequence, group, row block) to finish merges
+  // all splits of its rows
+  if (itm.n_splits > 1 && p.fuse_merge) {
+    const int row0 = itm.rblk * R_WG;
+    arrive_and_merge<DC>(p, p.counters + ((int64_t)b * (p.h_q / p.g) + j) * p.row_blocks + itm.rblk,
+                         reinterpret_cast<int*>(ring + 1024), b, j, row0, min(R_WG, p.rows - row0),
+                         itm.n_splits, itm.slot_base);
+  }
   return false;
 }
 

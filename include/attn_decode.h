@@ -69,8 +69,9 @@ typedef enum { ATTN_KIND_GQA = 0, ATTN_KIND_GTA = 1, ATTN_KIND_LATENT = 2 } attn
 /* Bits of the `flags` argument of the decode calls. */
 enum {
   ATTN_CAUSAL = 1,      /* q_len > 1: row t sees keys i <= L - q_len + t           */
-  ATTN_DEFER_MERGE = 2  /* leave split partials in the workspace; the caller runs
-                           attn_decode_merge (same stream) to finish the output    */
+  ATTN_DEFER_MERGE = 2  /* leave split partials in the workspace (plan->counters
+                           is not used); the caller runs attn_decode_merge (same
+                           stream) to finish the output                           */
 };
 
 /*
@@ -122,6 +123,16 @@ typedef struct {
  *   items   [n_items][4]  int32: b, group j, split index s, first token t0
  *           (the chunk is [t0, min(t0 + chunk, L_b)))
  *   seqinfo [batch][4]    int32: n_splits_b, partial slot base, L_b, chunk
+ *
+ * counters: with a non-NULL device array of attn_decode_counter_count()
+ * uint32 the streaming kernels merge split rows themselves (the last split
+ * workgroup of each (sequence, group, block of 64 query rows) to finish
+ * merges them, counted with atomic counters that wrap back to zero), so no
+ * merge launch follows.  The array must hold zeros before its first use;
+ * every complete call leaves it zero, so one array serves every later call
+ * and plan it is large enough for, as long as calls sharing it do not
+ * overlap.  NULL (what attn_decode_plan stores): the merge is a second
+ * launch on the stream.
  */
 typedef struct {
   int32_t n_items;
@@ -132,6 +143,7 @@ typedef struct {
   int32_t n_partial_slots; /* sum of n_splits_b over sequences with n_splits_b>1 */
   const int32_t* items;    /* DEVICE copy of items_host                          */
   const int32_t* seqinfo;  /* DEVICE copy of seqinfo_host                        */
+  uint32_t* counters;      /* DEVICE merge arrival counters or NULL (see below)  */
 } attn_plan_t;
 
 /*
@@ -170,11 +182,19 @@ int attn_decode_plan(const attn_shape_t* shape, const int32_t* seqlens_host, int
                      int max_items, attn_plan_t* plan);
 
 /*
- * Bytes of device workspace a decode call needs for split partials:
- * fp32 O_part [slots][q_len][h_q][d_v] followed by fp32 LSE_part
- * [slots][q_len][h_q], slots = plan->n_partial_slots (0 if nothing splits).
+ * Bytes of device workspace a decode call needs: fp32 O_part
+ * [slots][q_len][h_q][d_v] and fp32 LSE_part [slots][q_len][h_q] for split
+ * partials (slots = plan->n_partial_slots), then per-workgroup flags of the
+ * latent kernel's fix-up pass.  Contents need no initialisation.
  */
 size_t attn_decode_workspace_size(const attn_plan_t* plan, int h_q, int d_v);
+
+/*
+ * Number of uint32 merge counters (plan->counters) a call with this plan
+ * and h_q uses: batch * groups * ceil(rows / 64), rows = (h_q / groups) *
+ * q_len.  Returns 0 for an invalid plan.
+ */
+size_t attn_decode_counter_count(const attn_plan_t* plan, int h_q);
 
 /*
  * GQA decode (GTA/MQA/MHA-compatible layout with separate K and V pools).
@@ -184,7 +204,7 @@ size_t attn_decode_workspace_size(const attn_plan_t* plan, int h_q, int d_v);
  *   flags ATTN_CAUSAL and/or ATTN_DEFER_MERGE
  *   plan, workspace  from attn_decode_plan / attn_decode_workspace_size;
  *        the workspace must be 256-byte aligned (may be NULL if the plan
- *        splits nothing)
+ *        splits nothing and the kernel needs no flags)
  * Supported: d in {64, 128}; h_q % h_kv == 0; q_len in [1, 16].
  */
 int attn_decode_gqa(const attn_paged_kv_t* kv, const void* q, void* out, float* lse,

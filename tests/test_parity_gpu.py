@@ -213,3 +213,37 @@ def test_scores_far_above_first_tile(name):
                 np.array([min(40.0, i / 4.0)], np.float32))[0]
     inp.update(q=synth.round_bf16(q), pool0=lat)
     _check(w, inp, f"{name}/far", chunk_tokens=0)
+
+
+@pytest.mark.parametrize("name", ["gqa_llama8b", "gta_8k", "gla2", "mla_spec4"])
+def test_fused_merge_counters_return_to_zero(name):
+    """Split rows are merged inside the streaming kernels by the last split
+    workgroup of each row block, counted with wrapping counters: after every
+    call the counters are back to zero, one counter array serves consecutive
+    plans, and the result equals the separate merge launch bit for bit."""
+    w = SMALL[name]
+    inp = synth.make_inputs(w)
+    d = H.to_device(w, inp)
+    ref, ref_lse = oracle.decode(w, inp)
+    vmax = H.value_max(w, inp)
+    kw = dict(groups=w.groups, scale=w.softmax_scale, causal=w.causal,
+              rope_theta=w.rope_theta, d_rope=w.d_rope)
+    args = (w.kind, d["q"], d["pool0"], d["pool1"], d["rope"], d["page_table"], d["seqlens"],
+            d["seqlens_host"])
+    counters = None
+    for chunk in (64, 192, 128):
+        plan = binding.DevicePlan(
+            binding.shape(w.kind, binding.ATTN_BF16, w.batch, w.q_len, w.h_q, w.groups,
+                          w.head_dim, w.d_rope, w.page_size, w.causal),
+            d["seqlens_host"], d["q"].device, chunk_tokens=chunk)
+        if counters is None:
+            counters = plan.counters
+        plan.plan.counters = counters.data_ptr()  # one array for every plan
+        out, lse, _, _ = binding.decode(*args, plan=plan, **kw)
+        sep, sep_lse, _, _ = binding.decode(*args, chunk_tokens=chunk, fused_merge=False, **kw)
+        torch.cuda.synchronize()
+        print(f"[fused] {name} chunk={chunk} splits={plan.plan.max_splits}", flush=True)
+        assert plan.plan.max_splits > 1
+        H.compare(H.to_np(out), H.to_np(lse), ref, ref_lse, vmax, f"{name}/fused{chunk}")
+        assert torch.equal(out, sep) and torch.equal(lse, sep_lse)
+        assert int(counters.count_nonzero()) == 0
