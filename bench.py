@@ -155,6 +155,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--chunk-tokens", type=int, default=0, help="force the split chunk size")
+    ap.add_argument("--merge", choices=["fused", "launch"], default="launch",
+                    help="launch: a merge launch after the decode (faster here); fused: "
+                         "the decode kernel merges split rows itself (plan counters)")
     ap.add_argument("--plan-mem", choices=["device", "host"], default="device",
                     help="device: copy each step's plan to HBM; host: kernels read it from "
                          "pinned host memory")
@@ -209,7 +212,8 @@ def main():
     shp = binding.shape(w.kind, kv.dtype, B, T, H, w.groups, w.head_dim, w.d_rope, w.page_size,
                         w.causal)
     cu = torch.cuda.get_device_properties(dev).multi_processor_count
-    flags = (binding.ATTN_CAUSAL if w.causal else 0) | binding.ATTN_DEFER_MERGE
+    fused = args.merge == "fused"
+    flags = (binding.ATTN_CAUSAL if w.causal else 0) | (0 if fused else binding.ATTN_DEFER_MERGE)
 
     max_items = binding.attn_decode_plan_max_items(B, w.groups, int(max(1, seqlens_host.max())))
     # two pinned host plan buffers (a step rewrites one while the other may
@@ -239,11 +243,12 @@ def main():
             base = dev_buf.data_ptr()
         plan.seqinfo = base
         plan.items = base + B * 16
-        nonlocal counters
-        if counters is None:
-            counters = torch.zeros(max(1, binding.attn_decode_counter_count(plan, H)),
-                                   dtype=torch.int32, device=dev)
-        plan.counters = counters.data_ptr()
+        if fused:
+            nonlocal counters
+            if counters is None:
+                counters = torch.zeros(max(1, binding.attn_decode_counter_count(plan, H)),
+                                       dtype=torch.int32, device=dev)
+            plan.counters = counters.data_ptr()
         return plan, i
 
     plan0, _ = make_plan(0)
@@ -257,10 +262,11 @@ def main():
     s = stream.cuda_stream
 
     def step(k, evs, inner):
-        """One step: plan (host) + upload, decode, merge.  evs = [start,
-        before decode, after decode, end]; the inner two are recorded only
-        when `inner` (each recorded event costs the stream a few
-        microseconds, so steps without them give the step time)."""
+        """One step: plan (host) + upload, decode (which merges split rows
+        itself, or a merge launch after it).  evs = [start, before decode,
+        after decode, end]; the inner two are recorded only when `inner`
+        (each recorded event costs the stream a few microseconds, so steps
+        without them give the step time)."""
         evs[0].record(stream)
         plan, slot = make_plan(k)
         if inner:
@@ -281,11 +287,15 @@ def main():
             raise binding.AttnError(st, "decode")
         if inner:
             evs[2].record(stream)
-        st = binding.attn_decode_merge(plan, H, d_v, kv.dtype, ws.data_ptr(), ws_bytes,
-                                       out.data_ptr(), lse.data_ptr(), s)
-        if st != binding.ATTN_OK:
-            raise binding.AttnError(st, "merge")
-        evs[3].record(stream)
+        if not fused:
+            st = binding.attn_decode_merge(plan, H, d_v, kv.dtype, ws.data_ptr(), ws_bytes,
+                                           out.data_ptr(), lse.data_ptr(), s)
+            if st != binding.ATTN_OK:
+                raise binding.AttnError(st, "merge")
+        if inner and fused:
+            evs[3] = evs[2]  # the step ends with the decode kernel
+        else:
+            evs[3].record(stream)
         released[slot] = evs[3]
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
@@ -313,7 +323,7 @@ def main():
     inst = [e for e, f in zip(evs, inner) if f] or evs[:0]
     if inst:
         dec_ms = np.array([e[1].elapsed_time(e[2]) for e in inst])
-        merge_ms = np.array([e[2].elapsed_time(e[3]) for e in inst])
+        merge_ms = np.array([e[2].elapsed_time(e[3]) if e[3] is not e[2] else 0.0 for e in inst])
         inst_step_ms = np.array([e[0].elapsed_time(e[3]) for e in inst])
     else:  # a single timed step: its whole time stands for the kernel
         dec_ms = merge_ms = inst_step_ms = step_ms
@@ -348,7 +358,8 @@ def main():
                        "head_dim": w.head_dim, "d_rope": w.d_rope,
                        "mean_seqlen": float(seqlens_host.mean()), "page_size": w.page_size,
                        "kv_bytes_per_step": int(kvb), "gpus": 1, "layout": args.layout,
-                       "cache_flush": args.flush, "plan_mem": args.plan_mem},
+                       "cache_flush": args.flush, "plan_mem": args.plan_mem,
+                       "merge": args.merge},
             "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
             "tokens_per_s": round(tokens / (ms * 1e-3), 1),
             "step_ms_median": round(float(np.median(step_ms)), 5),

@@ -199,7 +199,7 @@ class DevicePlan:
     """A host plan plus its device copy (keeps the device arrays alive)."""
 
     def __init__(self, shape_: Shape, seqlens_host, device, cu_count=256, chunk_tokens=0,
-                 fused_merge=True):
+                 fused_merge=False):
         import torch
 
         seqlens_host = np.ascontiguousarray(seqlens_host, dtype=np.int32)
@@ -218,8 +218,8 @@ class DevicePlan:
         self.seqinfo_dev = torch.from_numpy(self.seqinfo_host).to(device)
         plan.items = self.items_dev.data_ptr()
         plan.seqinfo = self.seqinfo_dev.data_ptr()
-        # merge counters, zero-filled once; with them the streaming kernels
-        # merge split rows themselves
+        # optional merge counters, zero-filled once; with them the streaming
+        # kernels merge split rows themselves (one launch instead of two)
         self.counters = None
         if fused_merge:
             n = attn_decode_counter_count(plan, shape_.h_q)
@@ -231,14 +231,15 @@ class DevicePlan:
 def decode(kind: str, q, pool0, pool1, rope, page_table, seqlens, seqlens_host, *, groups: int,
            scale: float, causal: bool = False, rope_theta: float = 0.0, d_rope: int = 0,
            out=None, lse=None, chunk_tokens: int = 0, cu_count: int = 256, plan=None,
-           workspace=None, stream=None, defer_merge: bool = False, fused_merge: bool = True):
+           workspace=None, stream=None, defer_merge: bool = False, fused_merge: bool = False):
     """Run one decode through the native library on torch tensors.
 
     kind: "gqa" | "gta" | "latent".  q [B, T, H, Dq]; pools as in the header.
     Returns (out, lse, plan, workspace) so callers can reuse plan/workspace.
     With ``defer_merge`` the split partials stay in the workspace and the
-    caller finishes with ``merge``.  A new plan carries merge counters unless
-    ``fused_merge`` is false (then the merge is a second launch).
+    caller finishes with ``merge``.  With ``fused_merge`` a new plan carries
+    merge counters and the decode kernel merges split rows itself; otherwise
+    the merge is a second launch on the stream.
     """
     import torch
 

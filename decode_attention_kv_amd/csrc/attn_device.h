@@ -98,6 +98,22 @@ __device__ __forceinline__ int sload_i32(const int32_t* ptr) {
   return v;
 }
 
+// Split partials that the streaming kernels merge themselves are stored and
+// loaded with agent-scope relaxed atomics: on gfx950 these carry the sc1
+// scope bit, so they are written through / read past the per-XCD L2s and
+// need no cache-wide write-back or invalidate fence (the splits of one row
+// block may run on different XCDs).
+__device__ __forceinline__ void store_partial(float* dst, float v) {
+  __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_partial4(float* dst, f32x4 v) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) store_partial(dst + i, v[i]);
+}
+__device__ __forceinline__ float load_partial(const float* src) {
+  return __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Merge of split partials (Hydragen's softmax-denominator decomposition on
 // the "Efficient Inference" tag page) for rows [row0, row0 + nrows) of group
 // j of sequence b: M = max_s lse_s, w_s = exp(lse_s - M),
@@ -114,15 +130,16 @@ __device__ __forceinline__ void merge_split_rows(const Params& p, int b, int j, 
     const int hq = j * p.g + (r - tq * p.g);
     float M = -INFINITY;
     for (int s = 0; s < n_splits; ++s)
-      M = fmaxf(M, p.lse_part[((int64_t)(slot_base + s) * p.q_len + tq) * p.h_q + hq]);
+      M = fmaxf(M, load_partial(p.lse_part + ((int64_t)(slot_base + s) * p.q_len + tq) * p.h_q + hq));
     const float Ms = (M == -INFINITY) ? 0.f : M;
     f32x4 a = {0.f, 0.f, 0.f, 0.f};
     float W = 0.f;
     for (int s = 0; s < n_splits; ++s) {
       const int64_t pr = ((int64_t)(slot_base + s) * p.q_len + tq) * p.h_q + hq;
-      const float wt = __expf(p.lse_part[pr] - Ms);
+      const float wt = __expf(load_partial(p.lse_part + pr) - Ms);
       W += wt;
-      a += wt * *reinterpret_cast<const f32x4*>(p.o_part + pr * DV + c4);
+      const float* o = p.o_part + pr * DV + c4;
+      a += wt * f32x4{load_partial(o), load_partial(o + 1), load_partial(o + 2), load_partial(o + 3)};
     }
     const float inv = W > 0.f ? 1.f / W : 0.f;
     const int64_t orow = ((int64_t)b * p.q_len + tq) * p.h_q + hq;
@@ -134,21 +151,21 @@ __device__ __forceinline__ void merge_split_rows(const Params& p, int b, int j, 
   }
 }
 
-// After this workgroup wrote its split's partials: count its arrival on
-// `counter`; the last of the n_splits arrivals (atomicInc wraps the counter
-// to zero) merges the rows.  `is_last` is a workgroup-shared int.
+// After this workgroup stored its split's partials (store_partial): once
+// every thread's stores completed, count the arrival on `counter`; the last
+// of the n_splits arrivals (the counter wraps to zero) merges the rows.
+// `is_last` is a workgroup-shared int.
 template <int DV>
 __device__ __forceinline__ void arrive_and_merge(const Params& p, uint32_t* counter, int* is_last,
                                                  int b, int j, int row0, int nrows, int n_splits,
                                                  int slot_base) {
-  __threadfence();  // this workgroup's partials are visible device-wide
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores are complete
   __syncthreads();
-  if (threadIdx.x == 0) *is_last = atomicInc(counter, (unsigned)(n_splits - 1)) == (unsigned)(n_splits - 1);
+  if (threadIdx.x == 0)
+    *is_last = __builtin_amdgcn_atomic_inc32(counter, (uint32_t)(n_splits - 1), __ATOMIC_RELAXED,
+                                             "agent") == (uint32_t)(n_splits - 1);
   __syncthreads();
-  if (*is_last) {
-    __threadfence();  // and so are every other split's
-    merge_split_rows<DV>(p, b, j, row0, nrows, n_splits, slot_base);
-  }
+  if (*is_last) merge_split_rows<DV>(p, b, j, row0, nrows, n_splits, slot_base);
 }
 
 // Launchers, one per kernel family (each in its own translation unit).

@@ -568,6 +568,8 @@ __global__ __launch_bounds__(NW * 64) void decode_narrow(Params p) {
             __bf16 v4[4] = {(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
             *reinterpret_cast<uint2*>(reinterpret_cast<__bf16*>(p.out) + orow * D + dv) =
                 __builtin_bit_cast(uint2, v4);
+          } else if (p.fuse_merge) {
+            store_partial4(p.o_part + prow * D + dv, o);
           } else {
             *reinterpret_cast<f32x4*>(p.o_part + prow * D + dv) = o;
           }
@@ -578,6 +580,8 @@ __global__ __launch_bounds__(NW * 64) void decode_narrow(Params p) {
     if (row_ok[rt] && wave == 0 && grp == 0) {
       if (n_splits <= 1) {
         if (p.lse) p.lse[orow] = lse_val;
+      } else if (p.fuse_merge) {
+        store_partial(p.lse_part + prow, lse_val);
       } else {
         p.lse_part[prow] = lse_val;
       }

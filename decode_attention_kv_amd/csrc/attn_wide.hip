@@ -467,10 +467,16 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
       const int64_t prow =
           (int64_t)((itm.slot_base + itm.split) * p.q_len + tq[rt]) * p.h_q + hq[rt];
       float* o = p.o_part + prow * DC + dv0;
+      if (p.fuse_merge) {
 #pragma unroll
-      for (int dt = 0; dt < G::NDVH; ++dt)
-        *reinterpret_cast<f32x4*>(o + dt * 16) = acc[rt][dt] * inv;
-      if (kh == 0 && grp == 0) p.lse_part[prow] = lse_val;
+        for (int dt = 0; dt < G::NDVH; ++dt) store_partial4(o + dt * 16, acc[rt][dt] * inv);
+        if (kh == 0 && grp == 0) store_partial(p.lse_part + prow, lse_val);
+      } else {
+#pragma unroll
+        for (int dt = 0; dt < G::NDVH; ++dt)
+          *reinterpret_cast<f32x4*>(o + dt * 16) = acc[rt][dt] * inv;
+        if (kh == 0 && grp == 0) p.lse_part[prow] = lse_val;
+      }
     }
   }
   // the last split of this (sequence, group, row block) to finish merges

@@ -235,7 +235,7 @@ def test_fused_merge_counters_return_to_zero(name):
         plan = binding.DevicePlan(
             binding.shape(w.kind, binding.ATTN_BF16, w.batch, w.q_len, w.h_q, w.groups,
                           w.head_dim, w.d_rope, w.page_size, w.causal),
-            d["seqlens_host"], d["q"].device, chunk_tokens=chunk)
+            d["seqlens_host"], d["q"].device, chunk_tokens=chunk, fused_merge=True)
         if counters is None:
             counters = plan.counters
         plan.plan.counters = counters.data_ptr()  # one array for every plan
