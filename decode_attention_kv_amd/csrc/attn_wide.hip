@@ -165,47 +165,62 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
   const uint32_t ring_base = lds_u32(ring);
   const int64_t head_off = (int64_t)j * p.head_stride;
 
-  // this wave's loads of tile t (clamped to the last tile) into stage u
-  auto issue = [&](int t, int u) {
+  // This wave's loads of tile t (clamped to the last tile) into stage u:
+  // `prepare` looks up the page and forms the bases, `issue_load` issues
+  // load k of a full tile, `issue_clamped` all loads of a partial tile.
+  constexpr int LK = G::LLOADS / NW, RK = G::RLOADS / NW;
+  constexpr int RPB = G::PAIR ? 2 : 1;   // rows per latent block
+  struct Fetch {
+    const char* lbase;
+    const char* rbase;
+    uint32_t sbase;
+    int valid;  // rows of the tile that exist
+  };
+  auto prepare = [&](int t, int u) __attribute__((always_inline)) {
     const int tt = min(t, n_tiles - 1);
     const int key0 = t0 + tt * 64;                  // 64-aligned, inside one page
     const int64_t page = tt < PT_MAX ? __builtin_amdgcn_readfirstlane(ptab[tt])
                                      : sload_i32(pt_row + (key0 >> p.page_shift));
     const int slot0 = key0 & pmask;
-    const int valid = min(64, t_end - key0);        // rows of the tile that exist
-    const char* lbase = uniform_ptr(
+    Fetch f;
+    f.valid = min(64, t_end - key0);
+    f.lbase = uniform_ptr(
         p.pool0 + (page * p.page_stride + (int64_t)slot0 * p.token_stride + head_off) * 2);
-    const char* rbase =
+    f.rbase =
         uniform_ptr(p.rope + (page * p.rpage_stride + (int64_t)slot0 * p.rtoken_stride) * 2);
-    const uint32_t sbase = ring_base + u * G::STAGE;
-    constexpr int LK = G::LLOADS / NW, RK = G::RLOADS / NW;
-    constexpr int RPB = G::PAIR ? 2 : 1;   // rows per latent block
-    if (valid == 64) {
+    f.sbase = ring_base + u * G::STAGE;
+    return f;
+  };
+  auto issue_load = [&](const Fetch& f, int k) __attribute__((always_inline)) {
+    const int blk = wave + NW * (k < LK ? k : k - LK);
+    if (k < LK)
+      dma16(f.lbase + (int64_t)blk * RPB * lts2, vlat, f.sbase + blk * G::BSTR);
+    else
+      dma16(f.rbase + (int64_t)blk * 8 * rts2, vrope, f.sbase + G::R_OFF + blk * 1024);
+  };
+  // a partial last tile: rows past the end re-read the last row, so that
+  // stale cache contents never reach the MFMAs
+  auto issue_clamped = [&](const Fetch& f) __attribute__((always_inline)) {
 #pragma unroll
-      for (int k = 0; k < LK; ++k) {
-        const int blk = wave + NW * k;
-        dma16(lbase + (int64_t)blk * RPB * lts2, vlat, sbase + blk * G::BSTR);
-      }
+    for (int k = 0; k < LK; ++k) {
+      const int blk = wave + NW * k;
+      const int r = min(blk * RPB + lrow, f.valid - 1);
+      dma16(f.lbase, (uint32_t)(r * lts2 + lunit * 16), f.sbase + blk * G::BSTR);
+    }
 #pragma unroll
-      for (int k = 0; k < RK; ++k) {
-        const int blk = wave + NW * k;
-        dma16(rbase + (int64_t)blk * 8 * rts2, vrope, sbase + G::R_OFF + blk * 1024);
-      }
+    for (int k = 0; k < RK; ++k) {
+      const int blk = wave + NW * k;
+      const int r = min(blk * 8 + rrow, f.valid - 1);
+      dma16(f.rbase, (uint32_t)(r * rts2 + runit * 16), f.sbase + G::R_OFF + blk * 1024);
+    }
+  };
+  auto issue = [&](int t, int u) __attribute__((always_inline)) {
+    const Fetch f = prepare(t, u);
+    if (f.valid == 64) {
+#pragma unroll
+      for (int k = 0; k < LPW; ++k) issue_load(f, k);
     } else {
-      // a partial last tile: rows past the end re-read the last row, so
-      // that stale cache contents never reach the MFMAs
-#pragma unroll
-      for (int k = 0; k < LK; ++k) {
-        const int blk = wave + NW * k;
-        const int r = min(blk * RPB + lrow, valid - 1);
-        dma16(lbase, (uint32_t)(r * lts2 + lunit * 16), sbase + blk * G::BSTR);
-      }
-#pragma unroll
-      for (int k = 0; k < RK; ++k) {
-        const int blk = wave + NW * k;
-        const int r = min(blk * 8 + rrow, valid - 1);
-        dma16(rbase, (uint32_t)(r * rts2 + runit * 16), sbase + G::R_OFF + blk * 1024);
-      }
+      issue_clamped(f);
     }
   };
 
@@ -259,13 +274,19 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
   }
   bool over = false;
 
+  float neg_m[RT];  // -(reference max), fixed after the first tile
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) neg_m[rt] = 0.f;
+
   if (n_tiles > 0) {
 #pragma unroll
     for (int u = 0; u < STAGES - 1; ++u) issue(u, u);
   }
 
-  for (int t = 0; t < n_tiles; ++t) {
-    const int u = t % STAGES;
+  // One tile in stage U (a compile-time constant, so every LDS operand
+  // address is a per-lane base plus an immediate).
+  auto tile = [&](int t, auto ucst) __attribute__((always_inline)) {
+    constexpr int U = decltype(ucst)::value;
     {
       constexpr int ahead = (STAGES - 2) * LPW;
       __builtin_amdgcn_s_waitcnt((ahead & 15) | ((ahead >> 4) << 14) | (0x7 << 4) | (0xf << 8));
@@ -273,8 +294,12 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
     // every wave's loads of tile t have landed, and every wave is done with
     // tile t - 1 (its stage and the probability buffer are free again)
     __syncthreads();
-    issue(t + STAGES - 1, (t + STAGES - 1) % STAGES);
-    const char* sb = ring + u * G::STAGE;
+    // refill the stage of tile t - 1 with tile t + STAGES - 1: a full tile's
+    // loads are spread over the score MFMAs below, a partial one's issued now
+    const Fetch nf = prepare(t + STAGES - 1, (U + STAGES - 1) % STAGES);
+    const bool spread = nf.valid == 64;
+    if (!spread) issue_clamped(nf);
+    const char* sb = ring + U * G::STAGE;
     const int key0 = t0 + t * 64;
 
     // scores S^T for this wave's 32 keys: 2 M tiles x RT row tiles.  The K
@@ -285,8 +310,9 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
     for (int rt = 0; rt < RT; ++rt) sa[rt][0] = sa[rt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
     {
       constexpr int NS = 2 * G::NKC;   // step = (chunk c, M tile mt)
+      static_assert(NS >= 2 * LPW, "every load finds a step");
       constexpr int KD = 6;
-      auto kread = [&](int st) {
+      auto kread = [&](int st) __attribute__((always_inline)) {
         const int c = st >> 1, mt = st & 1;
         const char* src;
         if (c < G::NKL)
@@ -308,37 +334,43 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
           sa[rt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[st % KD], qreg[rt][c], sa[rt][mt],
                                                                0, 0, 0);
         if (st + KD < NS) kb[st % KD] = kread(st + KD);
+        if ((st & 1) && (st >> 1) < LPW && spread) issue_load(nf, st >> 1);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
 
-    // mask; lane holds keys key0 + 32 kh + 16 mt + 4 grp + i of row col
+    // x = scale * score - m_ref (log2 units); lane holds keys
+    // key0 + 32 kh + 16 mt + 4 grp + i of row col.  Masked keys of a partial
+    // or causal tile: key - (key0 + 32 kh + 4 grp) = 16 mt + i must stay
+    // below the row's limit min(t_end, qlimit + 1) - (key0 + 32 kh + 4 grp).
     const bool full = (key0 + 64 <= t_end) && !p.causal;
-    float s[RT][2][4], tmax[RT];
+    const int kbase = key0 + 32 * kh + 4 * grp;
+    float x[RT][2][4], tmax[RT];
+    const bool first = RESCALE || t == 0;
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+    for (int rt = 0; rt < RT; ++rt) {
+      const float nm = first ? 0.f : neg_m[rt];
+      const int lim = min(t_end, qlimit[rt] == 0x7fffffff ? t_end : qlimit[rt] + 1) - kbase;
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float v = sa[rt][mt][i] * p.scale_log2;
-          if (!full) {
-            const int key = key0 + 32 * kh + 16 * mt + 4 * grp + i;
-            if (!(key < t_end && key <= qlimit[rt])) v = -INFINITY;
-          }
-          s[rt][mt][i] = v;
+          float v = fmaf(sa[rt][mt][i], p.scale_log2, nm);
+          if (!full && !(16 * mt + i < lim)) v = -INFINITY;
+          x[rt][mt][i] = v;
         }
+    }
 
     // reference max shared by the pair (kh = 0, 1) of each row half: taken
     // on the first tile (every tile when rescaling)
-    if (RESCALE || t == 0) {
+    if (first) {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         float mx = -INFINITY;
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[rt][mt][i]);
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, x[rt][mt][i]);
         tmax[rt] = wave_max4(mx);
       }
       if (grp == 0) {
@@ -363,28 +395,33 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
         } else {
           m_ref[rt] = pair_max;
         }
+        neg_m[rt] = (m_ref[rt] == -INFINITY) ? 0.f : -m_ref[rt];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x[rt][mt][i] += neg_m[rt];
       }
     }
 
     bf16x8 pb[RT];
+    float xmax = -INFINITY;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      const float m_use = (m_ref[rt] == -INFINITY) ? 0.f : m_ref[rt];
       float psum = 0.f;
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float x = s[rt][mt][i] - m_use;
-          // a score more than 2^64 above the reference (log2 units)
-          if constexpr (!RESCALE) over |= x > 64.f;
-          const float e = __builtin_amdgcn_exp2f(x);
+          xmax = fmaxf(xmax, x[rt][mt][i]);
+          const float e = __builtin_amdgcn_exp2f(x[rt][mt][i]);
           psum += e;
           pb[rt][mt * 4 + i] = (__bf16)e;
         }
       l_run[rt] += psum;
       *reinterpret_cast<bf16x8*>(pbuf + p_wr + rt * 1024) = pb[rt];
     }
+    // a score more than 2^64 above the reference (log2 units)
+    if constexpr (!RESCALE) over |= xmax > 64.f;
     __syncthreads();  // both key halves' probabilities are in the buffer
 
     // O^T += V^T P^T over all 64 keys for this wave's value half; for the
@@ -401,7 +438,7 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
       // step = (kc, dt); the two V^T reads of a step run VD steps ahead
       constexpr int NP = 2 * G::NDVH;
       constexpr int VD = 4;
-      auto vread = [&](int st) {
+      auto vread = [&](int st) __attribute__((always_inline)) {
         const int kc = st / G::NDVH, dt = st % G::NDVH;
         constexpr int RS = G::PAIR ? 16 : 32;   // blocks per 32 keys
         const char* s0 = sb + (((dt >> 2) & 1) ? v_tr_m : v_tr_p) + kc * RS * G::BSTR + dt * 32;
@@ -424,6 +461,15 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
         if (st + VD < NP) vb[st % VD] = vread(st + VD);
         __builtin_amdgcn_sched_barrier(0);
       }
+    }
+  };
+
+  // the tile loop, unrolled by the ring depth
+  for (int t = 0; t < n_tiles; t += STAGES) {
+    tile(t, std::integral_constant<int, 0>{});
+    if (t + 1 < n_tiles) tile(t + 1, std::integral_constant<int, 1>{});
+    if constexpr (STAGES > 2) {
+      if (t + 2 < n_tiles) tile(t + 2, std::integral_constant<int, 2>{});
     }
   }
   __builtin_amdgcn_s_waitcnt(0);  // drain the clamped trailing loads
@@ -499,6 +545,7 @@ void decode_wide(Params p) {
   using G = Geo<DC, DR>;
   static_assert(STAGES * G::STAGE + 4 * RT * 1024 + PT_MAX * 4 <= 160 * 1024, "LDS");
   static_assert((STAGES - 2) * (G::LOADS / NW) <= 63, "vmcnt range");
+  static_assert(STAGES == 2 || STAGES == 3, "tile loop unrolled for 2 or 3 stages");
   __shared__ __attribute__((aligned(1024))) char ring[STAGES * G::STAGE + 4 * RT * 1024 + PT_MAX * 4];
 
   if constexpr (RESCALE) {
