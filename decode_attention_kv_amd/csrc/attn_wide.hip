@@ -7,13 +7,13 @@
 // tokens, or a block of them) and streams the rows of its chunk through a
 // ring of STAGES 64-key LDS stages filled by direct global->LDS loads.
 //
-// Work split inside a workgroup: wave (kh, rh) owns the row half rh
-// (16*RT rows) and
-//   * scores S^T = K Q^T for the key half kh of every tile (32 keys; its
+// Work split inside a workgroup of 2 KQ waves: wave (kq, rh) owns the row
+// half rh (16*RT rows) and
+//   * scores S^T = K Q^T for key part kq of every tile (64 / KQ keys; its
 //     rows' queries stay in registers as MFMA B operands),
-//   * O^T += V^T P^T for the value-column half kh of its rows over all 64
-//     keys of the tile; the probabilities of the other key half come from
-//     the partner wave (kh^1, rh) through a small LDS buffer.
+//   * O^T += V^T P^T for the value-column part kq of its rows over all 64
+//     keys of the tile; the probabilities of the other key parts come from
+//     the partner waves (kq', rh) through a small LDS buffer.
 // So every K element is read from LDS by two waves (one per row half) and
 // every V element by two (one per row half), half of what a split over rows
 // alone needs.
@@ -38,6 +38,16 @@
 // classic online rescaling (RESCALE = true).
 #include "attn_device.h"
 
+#ifndef WIDE_KQ256
+#define WIDE_KQ256 4
+#endif
+#ifndef WIDE_KD512
+#define WIDE_KD512 6
+#endif
+#ifndef WIDE_VD512
+#define WIDE_VD512 4
+#endif
+
 namespace attn_dev {
 namespace {
 namespace wide {
@@ -45,7 +55,6 @@ namespace wide {
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
 
-constexpr int NW = 4;  // waves: key half kh = wave & 1, row half rh = wave >> 1
 
 __device__ __forceinline__ uint32_t lds_u32(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)(p);
@@ -82,8 +91,6 @@ template <int DC, int DR> struct Geo {
   static constexpr int STAGE = R_OFF + RLOADS * 1024;
   static constexpr int NKC = (DC + DR) / 32;  // 32-dim k-chunks of a score
   static constexpr int NKL = DC / 32;         // ... of which latent
-  static constexpr int NDVH = DC / 32;        // 16-wide value tiles in one half
-  static_assert(LLOADS % NW == 0 && RLOADS % NW == 0, "loads split evenly over the waves");
   static_assert(R_OFF % 1024 == 0, "RoPE block alignment");
 };
 
@@ -96,9 +103,15 @@ constexpr int PT_MAX = 512;  // tiles whose page ids are kept in LDS
 
 // Stream the item's chunk and write its output rows; returns true, writing
 // nothing, when (RESCALE = false) some row outgrew its fixed reference.
-template <int DC, int DR, int RT, int STAGES, bool RESCALE>
+template <int DC, int DR, int RT, int STAGES, int KQ, bool RESCALE>
 __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* ring) {
   using G = Geo<DC, DR>;
+  constexpr int NW = 2 * KQ;           // waves: key part kq = wave % KQ, row half wave / KQ
+  constexpr int KPW = 64 / KQ;         // keys per wave per tile
+  constexpr int MT = KPW / 16;         // 16-key M tiles per wave
+  constexpr int NDVW = DC / 16 / KQ;   // 16-wide value tiles per wave
+  static_assert(KQ == 2 || KQ == 4, "key split");
+  static_assert(G::LLOADS % NW == 0 && G::RLOADS % NW == 0, "loads split evenly over the waves");
   constexpr int LPW = G::LOADS / NW;   // loads per wave per stage
   constexpr int R_WG = 32 * RT;        // rows per workgroup
   constexpr int PBUF = STAGES * G::STAGE;
@@ -107,7 +120,7 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int kh = wave & 1, rh = wave >> 1;
+  const int kq = wave % KQ, rh = wave / KQ;
   const int col = lane & 15;
   const int grp = lane >> 4;
   const int b = itm.b, j = itm.j, t0 = itm.t0, t_end = itm.t_end, n_tiles = itm.n_tiles;
@@ -225,52 +238,55 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
   };
 
   // per-lane operand bases inside a stage (bytes).  K operand of key row
-  // r = 32 kh + 16 mt + col, unit 4 c + grp: 512-wide rows sit at r * BSTR;
+  // r = KPW kq + 16 mt + col, unit 4 c + grp: 512-wide rows sit at r * BSTR;
   // 256-wide row r in block r / 2, half r % 2, unit XOR-ed with 8 (r % 2),
   // which moves unit 4 c + grp by +-8 units as bit 1 of c is clear / set
   int s_lat_p, s_lat_m;
   if constexpr (G::PAIR) {
     const int bb = col & 1;
-    const int base = (16 * kh + (col >> 1)) * G::BSTR + bb * 512 + grp * 16;
+    const int base = (KPW / 2 * kq + (col >> 1)) * G::BSTR + bb * 512 + grp * 16;
     s_lat_p = base + 128 * bb;
     s_lat_m = base - 128 * bb;
   } else {
-    s_lat_p = s_lat_m = (32 * kh + col) * G::BSTR + grp * 16;
+    s_lat_p = s_lat_m = (KPW * kq + col) * G::BSTR + grp * 16;
   }
   // RoPE operand: row r as above, unit (4 c + grp) XOR (r / 2) mod 8, for
   // the two RoPE k-chunks c = 0, 1
   const int rx = (col >> 1) & 7;
-  const int s_rope0 = G::R_OFF + (32 * kh + col) * 128 + ((grp) ^ rx) * 16;
-  const int s_rope1 = G::R_OFF + (32 * kh + col) * 128 + ((4 + grp) ^ rx) * 16;
+  const int s_rope0 = G::R_OFF + (KPW * kq + col) * 128 + ((grp) ^ rx) * 16;
+  const int s_rope1 = G::R_OFF + (KPW * kq + col) * 128 + ((4 + grp) ^ rx) * 16;
   // V^T operand (transposing reads): rows 32 kc + 4 grp + col / 4 (+16),
-  // value units 2 d + (col % 4) / 2 with d = kh NDVH + dt, byte half col % 2
+  // value units 2 d + (col % 4) / 2 with d = kq NDVW + dt, byte half col % 2;
+  // 256-wide rows move by +-8 units as bit 2 of d is clear / set, which is
+  // bit 2 of dt when NDVW is a multiple of 8 and bit 0 of kq when NDVW = 4
   int v_tr_p, v_tr_m;
   if constexpr (G::PAIR) {
     const int bb = (col >> 2) & 1;
     const int base = (2 * grp + (col >> 3)) * G::BSTR + bb * 512 + ((col & 3) >> 1) * 16 +
-                     (col & 1) * 8 + kh * G::NDVH * 32;
+                     (col & 1) * 8 + kq * NDVW * 32;
     v_tr_p = base + 128 * bb;
     v_tr_m = base - 128 * bb;
+    if (NDVW % 8 != 0 && (kq & 1)) v_tr_p = v_tr_m;
   } else {
     v_tr_p = v_tr_m = (4 * grp + (col >> 2)) * G::BSTR + ((col & 3) >> 1) * 16 + (col & 1) * 8 +
-                      kh * G::NDVH * 32;
+                      kq * NDVW * 32;
   }
-  // probability exchange: slot ((rh, kh), rt) of 1 KB, lane-linear
+  // probability exchange: slot (rh, 16-key block, rt) of 512 bytes, 8 bytes
+  // per lane; a 32-key chunk's B operand is blocks 2 kc and 2 kc + 1
   char* const pbuf = ring + PBUF;
-  const int p_wr = ((rh * 2 + kh) * RT) * 1024 + lane * 16;
-  const int p_rd = ((rh * 2) * RT) * 1024 + lane * 16;   // + (kc * RT + rt) * 1024
+  const int p_lane = rh * 4 * RT * 512 + lane * 8;   // + (block * RT + rt) * 512
   float* const tex = reinterpret_cast<float*>(pbuf);     // tile-max exchange (aliases pbuf)
-  const int t_wr = ((rh * 2 + kh) * RT) * 16 + col;
-  const int t_rd = ((rh * 2 + (kh ^ 1)) * RT) * 16 + col;
+  const int t_wr = ((rh * KQ + kq) * RT) * 16 + col;    // + rt * 16; partners kq'
+  const int t_rh = (rh * KQ * RT) * 16 + col;           // + (kq' * RT + rt) * 16
 
-  f32x4 acc[RT][G::NDVH];
+  f32x4 acc[RT][NDVW];
   float m_ref[RT], l_run[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     m_ref[rt] = -INFINITY;
     l_run[rt] = 0.f;
 #pragma unroll
-    for (int i = 0; i < G::NDVH; ++i) acc[rt][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < NDVW; ++i) acc[rt][i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   bool over = false;
 
@@ -283,10 +299,10 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
     for (int u = 0; u < STAGES - 1; ++u) issue(u, u);
   }
 
-  // One tile in stage U (a compile-time constant, so every LDS operand
-  // address is a per-lane base plus an immediate).
+  // One tile in stage U; when U is a compile-time constant every LDS operand
+  // address is a per-lane base plus an immediate.
   auto tile = [&](int t, auto ucst) __attribute__((always_inline)) {
-    constexpr int U = decltype(ucst)::value;
+    const int U = static_cast<int>(ucst);
     {
       constexpr int ahead = (STAGES - 2) * LPW;
       __builtin_amdgcn_s_waitcnt((ahead & 15) | ((ahead >> 4) << 14) | (0x7 << 4) | (0xf << 8));
@@ -302,18 +318,20 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
     const char* sb = ring + U * G::STAGE;
     const int key0 = t0 + t * 64;
 
-    // scores S^T for this wave's 32 keys: 2 M tiles x RT row tiles.  The K
+    // scores S^T for this wave's KPW keys: MT M tiles x RT row tiles.  The K
     // operand reads run KD steps ahead of the MFMAs that consume them
     // (scheduling fences keep that order)
-    f32x4 sa[RT][2];
+    f32x4 sa[RT][MT];
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) sa[rt][0] = sa[rt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) sa[rt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     {
-      constexpr int NS = 2 * G::NKC;   // step = (chunk c, M tile mt)
+      constexpr int NS = MT * G::NKC;  // step = (chunk c, M tile mt)
       static_assert(NS >= 2 * LPW, "every load finds a step");
-      constexpr int KD = 6;
+      constexpr int KD = DC >= 512 && RT > 1 ? WIDE_KD512 : 6;
       auto kread = [&](int st) __attribute__((always_inline)) {
-        const int c = st >> 1, mt = st & 1;
+        const int c = st / MT, mt = st % MT;
         const char* src;
         if (c < G::NKL)
           src = sb + (((c >> 1) & 1) ? s_lat_m : s_lat_p) +
@@ -328,7 +346,7 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
-        const int c = st >> 1, mt = st & 1;
+        const int c = st / MT, mt = st % MT;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
           sa[rt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[st % KD], qreg[rt][c], sa[rt][mt],
@@ -340,19 +358,19 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
     }
 
     // x = scale * score - m_ref (log2 units); lane holds keys
-    // key0 + 32 kh + 16 mt + 4 grp + i of row col.  Masked keys of a partial
-    // or causal tile: key - (key0 + 32 kh + 4 grp) = 16 mt + i must stay
-    // below the row's limit min(t_end, qlimit + 1) - (key0 + 32 kh + 4 grp).
+    // key0 + KPW kq + 16 mt + 4 grp + i of row col.  Masked keys of a partial
+    // or causal tile: key - (key0 + KPW kq + 4 grp) = 16 mt + i must stay
+    // below the row's limit min(t_end, qlimit + 1) - (key0 + KPW kq + 4 grp).
     const bool full = (key0 + 64 <= t_end) && !p.causal;
-    const int kbase = key0 + 32 * kh + 4 * grp;
-    float x[RT][2][4], tmax[RT];
+    const int kbase = key0 + KPW * kq + 4 * grp;
+    float x[RT][MT][4], tmax[RT];
     const bool first = RESCALE || t == 0;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       const float nm = first ? 0.f : neg_m[rt];
       const int lim = min(t_end, qlimit[rt] == 0x7fffffff ? t_end : qlimit[rt] + 1) - kbase;
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float v = fmaf(sa[rt][mt][i], p.scale_log2, nm);
@@ -361,14 +379,14 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
         }
     }
 
-    // reference max shared by the pair (kh = 0, 1) of each row half: taken
+    // reference max shared by the waves (kq = 0 .. KQ-1) of a row half: taken
     // on the first tile (every tile when rescaling)
     if (first) {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         float mx = -INFINITY;
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) mx = fmaxf(mx, x[rt][mt][i]);
         tmax[rt] = wave_max4(mx);
@@ -380,7 +398,11 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
       __syncthreads();
       float other[RT];
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) other[rt] = tex[t_rd + rt * 16];
+      for (int rt = 0; rt < RT; ++rt) {
+        other[rt] = -INFINITY;
+#pragma unroll
+        for (int k2 = 0; k2 < KQ; ++k2) other[rt] = fmaxf(other[rt], tex[t_rh + (k2 * RT + rt) * 16]);
+      }
       __syncthreads();  // the exchange slots alias the probability buffer
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
@@ -390,35 +412,36 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
           const float a = __builtin_amdgcn_exp2f(m_ref[rt] - ((m_new == -INFINITY) ? 0.f : m_new));
           l_run[rt] *= a;
 #pragma unroll
-          for (int dt = 0; dt < G::NDVH; ++dt) acc[rt][dt] *= a;
+          for (int dt = 0; dt < NDVW; ++dt) acc[rt][dt] *= a;
           m_ref[rt] = m_new;
         } else {
           m_ref[rt] = pair_max;
         }
         neg_m[rt] = (m_ref[rt] == -INFINITY) ? 0.f : -m_ref[rt];
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) x[rt][mt][i] += neg_m[rt];
       }
     }
 
-    bf16x8 pb[RT];
     float xmax = -INFINITY;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       float psum = 0.f;
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int mt = 0; mt < MT; ++mt) {
+        bf16x4 pb;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           xmax = fmaxf(xmax, x[rt][mt][i]);
           const float e = __builtin_amdgcn_exp2f(x[rt][mt][i]);
           psum += e;
-          pb[rt][mt * 4 + i] = (__bf16)e;
+          pb[i] = (__bf16)e;
         }
+        *reinterpret_cast<bf16x4*>(pbuf + p_lane + ((kq * MT + mt) * RT + rt) * 512) = pb;
+      }
       l_run[rt] += psum;
-      *reinterpret_cast<bf16x8*>(pbuf + p_wr + rt * 1024) = pb[rt];
     }
     // a score more than 2^64 above the reference (log2 units)
     if constexpr (!RESCALE) over |= xmax > 64.f;
@@ -427,21 +450,26 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
     // O^T += V^T P^T over all 64 keys for this wave's value half; for the
     // 32-key chunk kc the A operand holds keys 32 kc + 4 grp + e (e < 4)
     // and 32 kc + 16 + 4 grp + (e - 4), matching the B operand written by
-    // wave kh = kc
+    // waves kq with keys in that chunk
     {
       bf16x8 pk[2][RT];
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-          pk[kc][rt] = *reinterpret_cast<const bf16x8*>(pbuf + p_rd + (kc * RT + rt) * 1024);
+        for (int rt = 0; rt < RT; ++rt) {
+          const bf16x4 lo = *reinterpret_cast<const bf16x4*>(pbuf + p_lane + ((2 * kc) * RT + rt) * 512);
+          const bf16x4 hi =
+              *reinterpret_cast<const bf16x4*>(pbuf + p_lane + ((2 * kc + 1) * RT + rt) * 512);
+          pk[kc][rt] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
       // step = (kc, dt); the two V^T reads of a step run VD steps ahead
-      constexpr int NP = 2 * G::NDVH;
-      constexpr int VD = 4;
+      constexpr int NP = 2 * NDVW;
+      constexpr int VD = DC >= 512 && RT > 1 ? WIDE_VD512 : 4;
       auto vread = [&](int st) __attribute__((always_inline)) {
-        const int kc = st / G::NDVH, dt = st % G::NDVH;
+        const int kc = st / NDVW, dt = st % NDVW;
         constexpr int RS = G::PAIR ? 16 : 32;   // blocks per 32 keys
-        const char* s0 = sb + (((dt >> 2) & 1) ? v_tr_m : v_tr_p) + kc * RS * G::BSTR + dt * 32;
+        const char* s0 = sb + ((NDVW % 8 == 0 && ((dt >> 2) & 1)) ? v_tr_m : v_tr_p) +
+                         kc * RS * G::BSTR + dt * 32;
         const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(s0));
         const bf16x4 v1 =
             __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(s0 + RS / 2 * G::BSTR));
@@ -453,7 +481,7 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int st = 0; st < NP; ++st) {
-        const int kc = st / G::NDVH, dt = st % G::NDVH;
+        const int kc = st / NDVW, dt = st % NDVW;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
           acc[rt][dt] =
@@ -464,13 +492,20 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
     }
   };
 
-  // the tile loop, unrolled by the ring depth
-  for (int t = 0; t < n_tiles; t += STAGES) {
-    tile(t, std::integral_constant<int, 0>{});
-    if (t + 1 < n_tiles) tile(t + 1, std::integral_constant<int, 1>{});
-    if constexpr (STAGES > 2) {
-      if (t + 2 < n_tiles) tile(t + 2, std::integral_constant<int, 2>{});
+  // the tile loop, unrolled by the ring depth (constant stage addresses)
+  // except for 512-wide latents with two row tiles per wave, whose register
+  // budget does not hold two copies of the loop body
+  constexpr bool UNROLL = !(DC >= 512 && RT > 1);
+  if constexpr (UNROLL) {
+    for (int t = 0; t < n_tiles; t += STAGES) {
+      tile(t, std::integral_constant<int, 0>{});
+      if (t + 1 < n_tiles) tile(t + 1, std::integral_constant<int, 1>{});
+      if constexpr (STAGES > 2) {
+        if (t + 2 < n_tiles) tile(t + 2, std::integral_constant<int, 2>{});
+      }
     }
+  } else {
+    for (int t = 0; t < n_tiles; ++t) tile(t, t % STAGES);
   }
   __builtin_amdgcn_s_waitcnt(0);  // drain the clamped trailing loads
   __syncthreads();                // the ring is free
@@ -487,41 +522,46 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
   }
   __syncthreads();
   if constexpr (!RESCALE) {
-    if (flag[0] | flag[1] | flag[2] | flag[3]) return true;
+    int any = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) any |= flag[w];
+    if (any) return true;
   }
 
-  // ---- epilogue: lane holds O^T[dv = DC/2 kh + 16 dt + 4 grp + i][row]
+  // ---- epilogue: lane holds O^T[dv = DC/KQ kq + 16 dt + 4 grp + i][row]
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    const float l_row = lsum[rt] + lx[t_rd + rt * 16];
+    float l_row = 0.f;
+#pragma unroll
+    for (int k2 = 0; k2 < KQ; ++k2) l_row += lx[t_rh + (k2 * RT + rt) * 16];
     const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
     const float lse_val =
         l_row > 0.f ? (m_ref[rt] + __log2f(l_row)) * 0.69314718055994531f : -INFINITY;
     if (!row_ok[rt]) continue;
     const int64_t orow = (int64_t)(b * p.q_len + tq[rt]) * p.h_q + hq[rt];
-    const int dv0 = kh * (DC / 2) + grp * 4;
+    const int dv0 = kq * (DC / KQ) + grp * 4;
     if (itm.n_splits <= 1) {
       __bf16* o = reinterpret_cast<__bf16*>(p.out) + orow * DC + dv0;
 #pragma unroll
-      for (int dt = 0; dt < G::NDVH; ++dt) {
+      for (int dt = 0; dt < NDVW; ++dt) {
         __bf16 v4[4] = {(__bf16)(acc[rt][dt][0] * inv), (__bf16)(acc[rt][dt][1] * inv),
                         (__bf16)(acc[rt][dt][2] * inv), (__bf16)(acc[rt][dt][3] * inv)};
         *reinterpret_cast<uint2*>(o + dt * 16) = __builtin_bit_cast(uint2, v4);
       }
-      if (p.lse && kh == 0 && grp == 0) p.lse[orow] = lse_val;
+      if (p.lse && kq == 0 && grp == 0) p.lse[orow] = lse_val;
     } else {
       const int64_t prow =
           (int64_t)((itm.slot_base + itm.split) * p.q_len + tq[rt]) * p.h_q + hq[rt];
       float* o = p.o_part + prow * DC + dv0;
       if (p.fuse_merge) {
 #pragma unroll
-        for (int dt = 0; dt < G::NDVH; ++dt) store_partial4(o + dt * 16, acc[rt][dt] * inv);
-        if (kh == 0 && grp == 0) store_partial(p.lse_part + prow, lse_val);
+        for (int dt = 0; dt < NDVW; ++dt) store_partial4(o + dt * 16, acc[rt][dt] * inv);
+        if (kq == 0 && grp == 0) store_partial(p.lse_part + prow, lse_val);
       } else {
 #pragma unroll
-        for (int dt = 0; dt < G::NDVH; ++dt)
+        for (int dt = 0; dt < NDVW; ++dt)
           *reinterpret_cast<f32x4*>(o + dt * 16) = acc[rt][dt] * inv;
-        if (kh == 0 && grp == 0) p.lse_part[prow] = lse_val;
+        if (kq == 0 && grp == 0) p.lse_part[prow] = lse_val;
       }
     }
   }
@@ -530,7 +570,7 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
   if (itm.n_splits > 1 && p.fuse_merge) {
     const int row0 = itm.rblk * R_WG;
     arrive_and_merge<DC>(p, p.counters + ((int64_t)b * (p.h_q / p.g) + j) * p.row_blocks + itm.rblk,
-                         reinterpret_cast<int*>(ring + 1024), b, j, row0, min(R_WG, p.rows - row0),
+                         reinterpret_cast<int*>(ring + 4096), b, j, row0, min(R_WG, p.rows - row0),
                          itm.n_splits, itm.slot_base);
   }
   return false;
@@ -539,12 +579,12 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
 // RESCALE = false: the fixed-reference pass; records per workgroup whether
 // it had to give up (flags[block]).  RESCALE = true: the fix-up pass, a
 // second launch over the same grid that only works where the flag is set.
-template <int DC, int DR, int RT, int STAGES, bool RESCALE>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int DC, int DR, int RT, int STAGES, int KQ, bool RESCALE>
+__global__ __launch_bounds__(2 * KQ * 64) __attribute__((amdgpu_waves_per_eu(KQ / 2, KQ / 2)))
 void decode_wide(Params p) {
   using G = Geo<DC, DR>;
   static_assert(STAGES * G::STAGE + 4 * RT * 1024 + PT_MAX * 4 <= 160 * 1024, "LDS");
-  static_assert((STAGES - 2) * (G::LOADS / NW) <= 63, "vmcnt range");
+  static_assert((STAGES - 2) * (G::LOADS / (2 * KQ)) <= 63, "vmcnt range");
   static_assert(STAGES == 2 || STAGES == 3, "tile loop unrolled for 2 or 3 stages");
   __shared__ __attribute__((aligned(1024))) char ring[STAGES * G::STAGE + 4 * RT * 1024 + PT_MAX * 4];
 
@@ -573,7 +613,7 @@ void decode_wide(Params p) {
   itm.t_end = min(itm.t0 + chunk, itm.L);
   itm.n_tiles = (itm.t_end - itm.t0 + 63) / 64;
 
-  const bool gave_up = stream<DC, DR, RT, STAGES, RESCALE>(p, itm, ring);
+  const bool gave_up = stream<DC, DR, RT, STAGES, KQ, RESCALE>(p, itm, ring);
   if constexpr (!RESCALE) {
     if (threadIdx.x == 0) p.flags[blockIdx.x] = gave_up ? 1 : 0;
   }
@@ -581,28 +621,32 @@ void decode_wide(Params p) {
 
 }  // namespace wide
 
-template <int DC, int DR, int RT, int S>
+template <int DC, int DR, int RT, int S, int KQ>
 int launch_wide_one(Params p, int n_items, hipStream_t stream) {
   p.n_items = n_items;
   p.row_blocks = (p.rows + 32 * RT - 1) / (32 * RT);
   const int groups8 = (n_items + 7) / 8;
   const dim3 grid(groups8 * 8 * p.row_blocks);
-  hipLaunchKernelGGL((wide::decode_wide<DC, DR, RT, S, false>), grid, dim3(wide::NW * 64), 0,
+  hipLaunchKernelGGL((wide::decode_wide<DC, DR, RT, S, KQ, false>), grid, dim3(2 * KQ * 64), 0,
                      stream, p);
   // fix-up pass: exits at once unless the first pass flagged the workgroup
-  hipLaunchKernelGGL((wide::decode_wide<DC, DR, RT, S, true>), grid, dim3(wide::NW * 64), 0,
+  hipLaunchKernelGGL((wide::decode_wide<DC, DR, RT, S, KQ, true>), grid, dim3(2 * KQ * 64), 0,
                      stream, p);
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
 // Two row tiles per wave (64 rows per workgroup) unless the group has at
 // most 32 rows; as many 64-key stages as fit the LDS beside the probability
-// buffer (2 for 512-wide latents, 3 for 256-wide).
+// buffer (2 for 512-wide latents, 3 for 256-wide).  256-wide latents split
+// each tile's keys four ways over eight waves (two per SIMD, so one wave's
+// softmax and waits overlap another's MFMAs); 512-wide latents need the
+// register budget of one wave per SIMD and split keys two ways.
 template <int DC, int DR>
 int launch_wide(const Params& p, int n_items, hipStream_t stream) {
   constexpr int S = (DC >= 512) ? 2 : 3;
-  if (p.rows <= 32) return launch_wide_one<DC, DR, 1, S>(p, n_items, stream);
-  return launch_wide_one<DC, DR, 2, S>(p, n_items, stream);
+  constexpr int KQ = (DC >= 512) ? 2 : WIDE_KQ256;
+  if (p.rows <= 32) return launch_wide_one<DC, DR, 1, S, KQ>(p, n_items, stream);
+  return launch_wide_one<DC, DR, 2, S, KQ>(p, n_items, stream);
 }
 
 }  // namespace
