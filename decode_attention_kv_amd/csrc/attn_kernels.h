@@ -84,8 +84,8 @@ inline KernelChoice choose_kernel(const attn_shape_t& sh) {
     k.stages = sh.head_dim >= 512 ? 2 : 3;
     k.wgs_per_cu = 1;
     k.row_blocks = k.rows <= 32 ? 1 : (k.rows + 63) / 64;
-    k.rmax = 1.1;
-    k.fixed_tiles = 6.0;
+    k.rmax = 1.25;
+    k.fixed_tiles = 8.0;
     return k;
   }
   if (narrow) {
