@@ -84,6 +84,7 @@ inline KernelChoice choose_kernel(const attn_shape_t& sh) {
     k.stages = sh.head_dim >= 512 ? 2 : 3;
     k.wgs_per_cu = 1;
     k.row_blocks = k.rows <= 32 ? 1 : (k.rows + 63) / 64;
+    k.same_xcd_groups = true;  // groups share RoPE rows, row blocks latent rows
     k.rmax = 1.25;
     k.fixed_tiles = 8.0;
     return k;
@@ -111,8 +112,9 @@ inline KernelChoice choose_kernel(const attn_shape_t& sh) {
 
 // Workspace layout: fp32 O_part [slots][q_len][h_q][d_v] (256-byte padded),
 // fp32 LSE_part [slots][q_len][h_q] (256-byte padded), then one int32 flag
-// per workgroup of the latent streaming kernel (its grid is the items padded
-// to a multiple of 8 times at most ceil(rows / 64) row blocks).
+// per workgroup of the latent streaming kernel (its grid: the (sequence,
+// chunk) units padded to a multiple of 8, times groups, times at most
+// ceil(rows / 64) row blocks).
 inline size_t flags_offset(const attn_plan_t* plan, int h_q, int d_v) {
   const size_t rows = (size_t)plan->n_partial_slots * plan->q_len * h_q;
   return (rows * d_v * 4 + 255) / 256 * 256 + (rows * 4 + 255) / 256 * 256;
@@ -122,7 +124,11 @@ inline int64_t row_blocks_of(const attn_plan_t* plan, int h_q) {
   return (rows + 63) / 64 > 0 ? (rows + 63) / 64 : 1;
 }
 inline size_t flags_bytes(const attn_plan_t* plan, int h_q) {
-  const int64_t blocks = (plan->n_items + 7) / 8 * 8 * row_blocks_of(plan, h_q);
+  // grid of the latent streaming kernel: (sequence, chunk) units padded to
+  // a multiple of 8, times groups, times row blocks
+  const int64_t g = plan->n_groups > 0 ? plan->n_groups : 1;
+  const int64_t units = (plan->n_items + g - 1) / g;
+  const int64_t blocks = (units + 7) / 8 * 8 * g * row_blocks_of(plan, h_q);
   return ((size_t)blocks * 4 + 255) / 256 * 256;
 }
 // Merge arrival counters (plan->counters): one per (sequence, group, block

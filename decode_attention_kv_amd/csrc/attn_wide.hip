@@ -591,14 +591,22 @@ void decode_wide(Params p) {
   if constexpr (RESCALE) {
     if (p.flags[blockIdx.x] == 0) return;
   }
-  // item and row block, with row blocks of one item 8 apart (same XCD)
+  // Item and row block.  The plan lists the groups of one (sequence, chunk)
+  // consecutively; all their row blocks are mapped to blocks 8 apart, so
+  // they run on one XCD and share its L2 (the groups read the same RoPE key
+  // rows, the row blocks the same latent rows).
   const int rb_count = p.row_blocks;
+  const int n_groups = p.h_q / p.g;
+  const int per = n_groups * rb_count;   // workgroups of one (sequence, chunk)
   const int bid = blockIdx.x;
-  const int blk8 = bid / (8 * rb_count);
-  const int rem = bid - blk8 * 8 * rb_count;
+  const int blk8 = bid / (8 * per);
+  const int rem = bid - blk8 * 8 * per;
+  const int unit = blk8 * 8 + (rem & 7);
+  const int sub = rem >> 3;
+  const int jl = sub / rb_count;
   Item itm;
-  itm.rblk = rem >> 3;
-  const int item = blk8 * 8 + (rem & 7);
+  itm.rblk = sub - jl * rb_count;
+  const int item = unit * n_groups + jl;
   if (item >= p.n_items) return;
   const int32_t* it = p.items + 4 * item;
   itm.b = __builtin_amdgcn_readfirstlane(it[0]);
@@ -625,8 +633,9 @@ template <int DC, int DR, int RT, int S, int KQ>
 int launch_wide_one(Params p, int n_items, hipStream_t stream) {
   p.n_items = n_items;
   p.row_blocks = (p.rows + 32 * RT - 1) / (32 * RT);
-  const int groups8 = (n_items + 7) / 8;
-  const dim3 grid(groups8 * 8 * p.row_blocks);
+  const int n_groups = p.h_q / p.g;
+  const int units = (n_items + n_groups - 1) / n_groups;   // (sequence, chunk) pairs
+  const dim3 grid((units + 7) / 8 * 8 * n_groups * p.row_blocks);
   hipLaunchKernelGGL((wide::decode_wide<DC, DR, RT, S, KQ, false>), grid, dim3(2 * KQ * 64), 0,
                      stream, p);
   // fix-up pass: exits at once unless the first pass flagged the workgroup

@@ -145,7 +145,8 @@ def _ws_expect(plan, slots, h_q, d_v):
     pad = lambda x: (x + 255) // 256 * 256
     group_rows = h_q // plan.n_groups * plan.q_len
     row_blocks = max(1, -(-group_rows // 64))
-    flags = (plan.n_items + 7) // 8 * 8 * row_blocks * 4
+    units = -(-plan.n_items // plan.n_groups)
+    flags = -(-units // 8) * 8 * plan.n_groups * row_blocks * 4
     return pad(rows * d_v * 4) + pad(rows * 4) + pad(flags)
 
 
