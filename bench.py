@@ -76,11 +76,14 @@ def flops(w, seqlens):
 
 
 def kernel_family(w):
-    if w.kind == "latent" and w.dtype == "bf16" and w.page_size >= 64:
-        return "wide"
-    if w.dtype == "bf16" and w.page_size >= 64:
-        return "narrow"
-    return "general"
+    """Decode kernel family of a workload (the streaming kernels take bf16 at
+    any page size; the general kernel fp32 and the shapes they do not)."""
+    if w.dtype != "bf16":
+        return "general"
+    if w.kind == "latent":
+        return "wide" if w.d_rope == 64 and w.head_dim in (256, 512) else "general"
+    ok = (w.head_dim in (64, 128) if w.kind == "gqa" else (w.head_dim == 128 and w.d_rope == 64))
+    return "narrow" if ok and w.group_size * w.q_len <= 64 else "general"
 
 
 def kernel_sha(w):
@@ -110,6 +113,29 @@ def load_traffic(workload, sha):
         return float(vals["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def apply_overrides(w, items):
+    """Workload `w` with FIELD=VALUE overrides (typed like the field); the
+    name records them, so no committed counter run is attributed to it."""
+    import dataclasses
+    if not items:
+        return w
+    types = {f.name: f.type for f in dataclasses.fields(w)}
+    kw = {}
+    for it in items:
+        k, _, v = it.partition("=")
+        if k not in types or k == "name":
+            raise SystemExit(f"--set: unknown workload field {k!r}")
+        t = types[k] if isinstance(types[k], type) else \
+            {"int": int, "float": float, "bool": bool, "str": str}[types[k]]
+        kw[k] = (v.lower() in ("1", "true", "yes")) if t is bool else t(v)
+    if "seqlen_hi" in kw and "max_seqlen" not in kw:
+        kw["max_seqlen"] = max(w.max_seqlen, kw["seqlen_hi"])
+    if kw.get("q_len", w.q_len) > 1 and "causal" not in kw:
+        kw["causal"] = True
+    tag = ",".join(f"{k}={v}" for k, v in kw.items())
+    return w.with_(name=f"{w.name}[{tag}]", **kw)
 
 
 def cpu_baseline(w, inp, seconds):
@@ -161,6 +187,9 @@ def main():
     ap.add_argument("--plan-mem", choices=["device", "host"], default="device",
                     help="device: copy each step's plan to HBM; host: kernels read it from "
                          "pinned host memory")
+    ap.add_argument("--set", action="append", default=[], metavar="FIELD=VALUE",
+                    help="override a workload field (e.g. q_len=2, h_q=16, groups=1, "
+                         "page_size=1, batch=64); the result is then not the named workload")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -186,7 +215,7 @@ def main():
         print(json.dumps({"copy_calibration_bytes": n, "launches": 3}))
         return
 
-    w = synth.WORKLOADS[args.workload]
+    w = apply_overrides(synth.WORKLOADS[args.workload], args.set)
     print(f"[bench] drawing inputs for {w.name}", file=sys.stderr, flush=True)
     inp = synth.make_inputs(w)
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
@@ -353,7 +382,7 @@ def main():
             "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
-            "config": {"workload": f"{w.name}: {DESCRIPTIONS.get(w.name, w.name)}",
+            "config": {"workload": f"{w.name}: {DESCRIPTIONS.get(w.name.split('[')[0], w.name)}",
                        "batch": B, "q_len": T, "h_q": H, "groups": w.groups,
                        "head_dim": w.head_dim, "d_rope": w.d_rope,
                        "mean_seqlen": float(seqlens_host.mean()), "page_size": w.page_size,

@@ -86,6 +86,37 @@ __device__ __forceinline__ void rope_sincos(float pos, float hi, float lo, float
 // Scalar (SMEM) load of one int32 from a wave-uniform address, waited for in
 // the same asm block.  SMEM loads count on lgkmcnt, so looking up a page id
 // does not drain the vmcnt-tracked direct-to-LDS loads in flight.
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)(p);
+}
+
+// A wave-uniform 64-bit pointer, made explicit so it is allocated to SGPRs.
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return reinterpret_cast<const char*>(((uint64_t)hi << 32) | lo);
+}
+
+// Direct global->LDS loads for rows of small pages, issued from asm so that
+// the compiler neither drains vmcnt before unrelated LDS reads nor waits on
+// them itself (the kernels' own waits cover them).  dma16v: one 16-byte load
+// per lane from a per-lane 64-bit address, nontemporal (cache rows are read
+// once), lane l writing LDS bytes [lds + 16 l, lds + 16 l + 16).  dma4: one
+// 4-byte load per active lane from base + voff (page ids), lane l writing
+// LDS bytes [lds + 4 l, lds + 4 l + 4).
+__device__ __forceinline__ void dma16v(uint64_t addr, uint32_t lds) {
+  const uint32_t l = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" : : "v"(addr), "s"(l)
+               : "memory");
+}
+__device__ __forceinline__ void dma4(const char* base, uint32_t voff, uint32_t lds) {
+  const uint32_t l = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" : : "v"(voff), "s"(base),
+               "s"(l) : "memory");
+}
+
 __device__ __forceinline__ int sload_i32(const int32_t* ptr) {
   // the address is wave-uniform; readfirstlane makes that explicit so the
   // operand is allocated to SGPRs

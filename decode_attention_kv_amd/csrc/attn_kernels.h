@@ -68,13 +68,14 @@ inline KernelChoice choose_kernel(const attn_shape_t& sh) {
   const int elem = sh.dtype == ATTN_BF16 ? 2 : 4;
   k.token_bytes = (sh.kind == ATTN_KIND_GQA) ? 2LL * sh.head_dim * elem
                                              : (int64_t)(sh.head_dim + sh.d_rope) * elem;
-  bool narrow = sh.dtype == ATTN_BF16 && k.rows <= 64 && sh.page_size >= kTile &&
+  // any power-of-two page size: whole pages per 16-key slice (>= 16) or per
+  // 64-key tile (>= 64) share one page id, smaller pages take one per row
+  bool narrow = sh.dtype == ATTN_BF16 && k.rows <= 64 &&
                 ((sh.kind == ATTN_KIND_GQA && (sh.head_dim == 64 || sh.head_dim == 128)) ||
                  (sh.kind == ATTN_KIND_GTA && sh.head_dim == 128 && sh.d_rope == 64));
   // latent heads: the wide streaming kernel (reported through `narrow` too:
   // "streaming" rather than the general kernel)
-  const bool wide = sh.dtype == ATTN_BF16 && sh.kind == ATTN_KIND_LATENT &&
-                    sh.page_size >= kTile && sh.d_rope == 64 &&
+  const bool wide = sh.dtype == ATTN_BF16 && sh.kind == ATTN_KIND_LATENT && sh.d_rope == 64 &&
                     (sh.head_dim == 512 || sh.head_dim == 256);
   if (env_force_general()) narrow = false;
   k.narrow = narrow || (wide && !env_force_general());
@@ -91,6 +92,7 @@ inline KernelChoice choose_kernel(const attn_shape_t& sh) {
   }
   if (narrow) {
     k.stages = narrow_stages(sh.kind, sh.head_dim, sh.d_rope);
+    if (sh.page_size < 16) k.stages = k.stages >= 4 ? 4 : 2;  // small-page rings
     const int lds = k.stages * narrow_stage_bytes(sh.kind, sh.head_dim, sh.d_rope) + 2048;
     int w = 163840 / lds;
     k.wgs_per_cu = w < 1 ? 1 : w > 2 ? 2 : w;

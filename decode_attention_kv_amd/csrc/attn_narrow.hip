@@ -171,6 +171,25 @@ struct SliceDMA {
       off[i] = (uint32_t)(row[i] * token_stride * 2 + c * 16);
     }
   }
+  // pages smaller than a slice: byte offsets of this lane's rows from the
+  // pool base, each row key min(kw + row, t_last) in its own page (ids[] =
+  // page id per key of the slice, from LDS)
+  __device__ __forceinline__ void offsets_sp(uint64_t* o, const int* ids, int kw, int t_last,
+                                             int pmask, int64_t page_stride, int64_t token_stride,
+                                             int64_t head_off) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int key = min(kw + row[i], t_last);
+      o[i] = (uint64_t)(((int64_t)ids[row[i]] * page_stride + (int64_t)(key & pmask) * token_stride +
+                         head_off) * 2) +
+             (off[i] - (uint32_t)(row[i] * token_stride * 2));
+    }
+  }
+  __device__ __forceinline__ void issue_sp(char* dst, const char* base, const uint64_t* o) const {
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+#pragma unroll
+    for (int i = 0; i < N; ++i) dma16v(b + o[i], lds_u32(dst + i * 1024));
+  }
   // full slice: every row valid, contiguous within one page
   __device__ __forceinline__ void issue(char* dst, const char* base) const {
 #pragma unroll
@@ -191,7 +210,7 @@ struct SliceDMA {
   }
 };
 
-template <int KIND, int D, int DR, int RT, int STAGES>
+template <int KIND, int D, int DR, int RT, int STAGES, bool SP>
 __global__ __launch_bounds__(NW * 64) void decode_narrow(Params p) {
   using G = Geo<KIND, D, DR>;
   constexpr int DN = D - DR;          // key entries from the K / tied row
@@ -210,6 +229,10 @@ __global__ __launch_bounds__(NW * 64) void decode_narrow(Params p) {
   __shared__ __attribute__((aligned(1024))) char st5[STAGES > 5 ? G::STAGE_BYTES : 16];
   __shared__ float merge_m[NW][16 * RT], merge_l[NW][16 * RT];
   __shared__ int merge_last;
+  // pages smaller than a slice (SP): page ids of each wave's 16 keys of a
+  // tile, in a ring of STAGES + 1 slots, loaded STAGES tiles ahead
+  constexpr int PSLOTS = STAGES + 1;
+  __shared__ int pid[SP ? PSLOTS * NW * KW : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -272,8 +295,37 @@ __global__ __launch_bounds__(NW * 64) void decode_narrow(Params p) {
   dma0.init(p.token_stride, lane);
   if constexpr (KIND == GTA) dmar.init(p.rtoken_stride, lane);
 
+  // small pages: the page ids of this wave's 16 keys of tile x (clamped to
+  // the last tile, each key to the last row), one 4-byte load per lane
+  const char* const pt_base = uniform_ptr(reinterpret_cast<const char*>(pt_row));
+  auto issue_ids = [&](int x) {
+    const int kw = t0 + min(x, n_tiles - 1) * KTILE + wave * KW;
+    const uint32_t voff = (uint32_t)(min(kw + lane, t_last) >> p.page_shift) * 4u;
+    if (lane < KW) dma4(pt_base, voff, lds_u32(&pid[((x % PSLOTS) * NW + wave) * KW]));
+  };
+
   // issue this wave's loads of tile `t` (clamped to the last tile) into stage u
   auto issue = [&](int t, int u) {
+    if constexpr (SP) {
+      // every row from its own page (rows past the end re-read the last
+      // row); then the page ids of tile t + STAGES
+      const int kw = t0 + min(t, n_tiles - 1) * KTILE + wave * KW;
+      const int* ids = &pid[((t % PSLOTS) * NW + wave) * KW];
+      char* dst = stage(u) + wave * G::WAVE_BYTES;
+      uint64_t o[SliceDMA<G::ROW0>::N];
+      dma0.offsets_sp(o, ids, kw, t_last, pmask, p.page_stride, p.token_stride,
+                      (int64_t)j * p.head_stride);
+      dma0.issue_sp(dst + G::K_OFF, p.pool0, o);
+      if constexpr (KIND == GQA) {
+        dma0.issue_sp(dst + G::V_OFF, p.pool1, o);
+      } else {
+        uint64_t orr[SliceDMA<(DR > 0 ? G::ROWR : 16)>::N];
+        dmar.offsets_sp(orr, ids, kw, t_last, pmask, p.rpage_stride, p.rtoken_stride, 0);
+        dmar.issue_sp(dst + G::R_OFF, p.rope, orr);
+      }
+      issue_ids(t + STAGES);
+      return;
+    }
     const int tt = min(t, n_tiles - 1);
     const int key0 = t0 + tt * KTILE + wave * KW;   // 16-aligned, inside one page
     const int kc = min(key0, t_last);
@@ -346,12 +398,20 @@ __global__ __launch_bounds__(NW * 64) void decode_narrow(Params p) {
 
   // start the ring; then wait for the (older) query loads only, so no
   // query load is still pending when the streaming loop starts
+  if constexpr (SP) {
+    // the page ids of the first STAGES tiles; later tiles' ids travel with
+    // the cache loads, STAGES tiles ahead of them
+    if (n_tiles > 0) {
+      for (int x = 0; x < STAGES; ++x) issue_ids(x);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+  }
   if (n_tiles > 0) {
 #pragma unroll
     for (int u = 0; u < STAGES - 1; ++u) issue(u, u);
   }
   {
-    constexpr int ahead = (STAGES - 1) * G::LOADS;
+    constexpr int ahead = (STAGES - 1) * (G::LOADS + (SP ? 1 : 0));
     __builtin_amdgcn_s_waitcnt((ahead & 15) | ((ahead >> 4) << 14) | (0x7 << 4) | (0xf << 8));
   }
 
@@ -506,7 +566,7 @@ __global__ __launch_bounds__(NW * 64) void decode_narrow(Params p) {
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
         issue(t + u + STAGES - 1, (u + STAGES - 1) % STAGES);
         // wait until this tile's loads (issued STAGES-1 tiles ago) landed
-        constexpr int ahead = (STAGES - 1) * G::LOADS;
+        constexpr int ahead = (STAGES - 1) * (G::LOADS + (SP ? 1 : 0));
         __builtin_amdgcn_s_waitcnt((ahead & 15) | ((ahead >> 4) << 14) | (0x7 << 4) | (0xf << 8));
         compute(t + u, u);
       }
@@ -595,11 +655,11 @@ __global__ __launch_bounds__(NW * 64) void decode_narrow(Params p) {
 
 }  // namespace narrow
 
-template <int KIND, int D, int DR, int RT, int S>
+template <int KIND, int D, int DR, int RT, int S, bool SP = false>
 int launch_narrow_s(Params p, int n_items, int groups, hipStream_t stream) {
   using G = narrow::Geo<KIND, D, DR>;
   if constexpr (S * G::STAGE_BYTES + 4096 > 163840) {
-    return launch_narrow_s<KIND, D, DR, RT, S - 1>(p, n_items, groups, stream);
+    return launch_narrow_s<KIND, D, DR, RT, S - 1, SP>(p, n_items, groups, stream);
   } else {
     p.n_items = n_items;
     // GTA: the groups of one (sequence, chunk) share an XCD (its L2 serves
@@ -608,7 +668,7 @@ int launch_narrow_s(Params p, int n_items, int groups, hipStream_t stream) {
     const int gsz = KIND == GTA ? groups : 1;
     p.row_blocks = gsz;
     const int blocks = (n_items + 8 * gsz - 1) / (8 * gsz) * 8 * gsz;
-    hipLaunchKernelGGL((narrow::decode_narrow<KIND, D, DR, RT, S>), dim3(blocks),
+    hipLaunchKernelGGL((narrow::decode_narrow<KIND, D, DR, RT, S, SP>), dim3(blocks),
                        dim3(narrow::NW * 64), 0, stream, p);
     return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
   }
@@ -616,6 +676,11 @@ int launch_narrow_s(Params p, int n_items, int groups, hipStream_t stream) {
 
 template <int KIND, int D, int DR, int RT>
 int launch_narrow_rt(const Params& p, int n_items, int groups, int stages, hipStream_t stream) {
+  // pages of fewer than 16 tokens: per-row page ids, rings of 2 or 4 stages
+  if (p.page_shift < 4) {
+    return stages >= 4 ? launch_narrow_s<KIND, D, DR, RT, 4, true>(p, n_items, groups, stream)
+                       : launch_narrow_s<KIND, D, DR, RT, 2, true>(p, n_items, groups, stream);
+  }
   switch (stages) {
     case 2: return launch_narrow_s<KIND, D, DR, RT, 2>(p, n_items, groups, stream);
     case 3: return launch_narrow_s<KIND, D, DR, RT, 3>(p, n_items, groups, stream);

@@ -36,6 +36,15 @@
 // 2^64 (log2 units).  A workgroup that sees such a score writes nothing and
 // sets its flag; a second launch redoes exactly those workgroups with the
 // classic online rescaling (RESCALE = true).
+//
+// Pages of at least 64 tokens hold whole tiles: one page id per tile, from
+// an LDS table filled once per item.  Smaller pages (SP = true, any power of
+// two down to single-token pages) give every row its own page: each wave
+// loads the rows of 64 / (2 KQ) consecutive keys of a tile, and a 4-byte
+// direct-to-LDS load per lane brings those keys' page ids into a small
+// per-wave LDS ring a stage ahead of the cache loads that need them (the
+// offsets are spread over the lanes, and no scalar or vector wait sits
+// between a page-table read and its use).
 #include "attn_device.h"
 
 #ifndef WIDE_KQ256
@@ -56,17 +65,6 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
 
 
-__device__ __forceinline__ uint32_t lds_u32(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)(p);
-}
-
-// A wave-uniform 64-bit pointer, made explicit so it is allocated to SGPRs.
-__device__ __forceinline__ const char* uniform_ptr(const char* p) {
-  const uint64_t a = reinterpret_cast<uint64_t>(p);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-  return reinterpret_cast<const char*>(((uint64_t)hi << 32) | lo);
-}
 
 // One direct global->LDS 16-byte load per lane from base + voff (base in
 // SGPRs, voff a per-lane 32-bit byte offset); lane l writes LDS bytes
@@ -79,6 +77,7 @@ __device__ __forceinline__ void dma16(const char* base, uint32_t voff, uint32_t 
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt" : : "v"(voff), "s"(base),
                "s"(l) : "memory");
 }
+
 
 template <int DC, int DR> struct Geo {
   static_assert((DC == 256 || DC == 512) && DR == 64, "latent widths");
@@ -103,7 +102,7 @@ constexpr int PT_MAX = 512;  // tiles whose page ids are kept in LDS
 
 // Stream the item's chunk and write its output rows; returns true, writing
 // nothing, when (RESCALE = false) some row outgrew its fixed reference.
-template <int DC, int DR, int RT, int STAGES, int KQ, bool RESCALE>
+template <int DC, int DR, int RT, int STAGES, int KQ, bool RESCALE, bool SP>
 __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* ring) {
   using G = Geo<DC, DR>;
   constexpr int NW = 2 * KQ;           // waves: key part kq = wave % KQ, row half wave / KQ
@@ -116,6 +115,10 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
   constexpr int R_WG = 32 * RT;        // rows per workgroup
   constexpr int PBUF = STAGES * G::STAGE;
   constexpr int PTAB = PBUF + 4 * RT * 1024;   // page-id table
+  // small pages: wave w loads the rows of keys [KR w, KR w + KR) of a tile;
+  // their page ids sit in a ring of STAGES slots of NW x 64 bytes at PTAB
+  constexpr int KR = 64 / NW;
+  static_assert(!SP || (KR <= 16 && STAGES * NW * 64 <= PT_MAX * 4), "page-id ring");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -125,6 +128,7 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
   const int grp = lane >> 4;
   const int b = itm.b, j = itm.j, t0 = itm.t0, t_end = itm.t_end, n_tiles = itm.n_tiles;
   const int L = itm.L;
+  const int t_last = t_end - 1;
   const int pmask = (1 << p.page_shift) - 1;
   const int32_t* pt_row = p.page_table + (int64_t)b * p.max_pages;
 
@@ -165,18 +169,36 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
   const int rrow = lane >> 3;                                    // row within the load
   const int runit = (lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7);
   const uint32_t vrope = (uint32_t)(rrow * rts2 + runit * 16);
-  // page ids of the item's first PT_MAX tiles in an LDS table (later tiles
-  // look theirs up in the page table)
+  const uint32_t ring_base = lds_u32(ring);
+  const int64_t head_off = (int64_t)j * p.head_stride;
+
+  // small pages: the page ids of this wave's KR keys of tile x (clamped to
+  // the last tile, each key to the last row) into ring slot x % STAGES
+  const char* const pt_base = uniform_ptr(reinterpret_cast<const char*>(pt_row));
+  auto issue_ids = [&](int x) __attribute__((always_inline)) {
+    const int kw = t0 + min(x, n_tiles - 1) * 64 + KR * wave;
+    const uint32_t voff = (uint32_t)(min(kw + lane, t_last) >> p.page_shift) * 4u;
+    const uint32_t dst = ring_base + PTAB + ((x % STAGES) * NW + wave) * 64;
+    if (lane < KR) dma4(pt_base, voff, dst);
+  };
+
   int* const ptab = reinterpret_cast<int*>(ring + PTAB);
-  for (int tt = tid; tt < min(n_tiles, PT_MAX); tt += NW * 64)
-    ptab[tt] = pt_row[(t0 + tt * 64) >> p.page_shift];
+  if constexpr (SP) {
+    // the page ids of the first STAGES - 1 tiles; later tiles' ids travel
+    // with the cache loads, STAGES - 1 tiles ahead of them
+    if (n_tiles > 0) {
+      for (int x = 0; x < STAGES - 1; ++x) issue_ids(x);
+    }
+  } else {
+    // page ids of the item's first PT_MAX tiles in an LDS table (later
+    // tiles look theirs up in the page table)
+    for (int tt = tid; tt < min(n_tiles, PT_MAX); tt += NW * 64)
+      ptab[tt] = pt_row[(t0 + tt * 64) >> p.page_shift];
+  }
   // the query and page-id loads must be complete before the asm loads
   // start counting, and the page-id table visible to every wave
   __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
   __syncthreads();
-
-  const uint32_t ring_base = lds_u32(ring);
-  const int64_t head_off = (int64_t)j * p.head_stride;
 
   // This wave's loads of tile t (clamped to the last tile) into stage u:
   // `prepare` looks up the page and forms the bases, `issue_load` issues
@@ -227,13 +249,82 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
       dma16(f.rbase, (uint32_t)(r * rts2 + runit * 16), f.sbase + G::R_OFF + blk * 1024);
     }
   };
-  auto issue = [&](int t, int u) __attribute__((always_inline)) {
-    const Fetch f = prepare(t, u);
-    if (f.valid == 64) {
+  // Small pages: every row's address from its own page id (rows past the
+  // end re-read the last row).  512-wide rows: one row per load, a uniform
+  // address formed at issue from the ids held by lanes 0..KR-1; 256-wide
+  // row pairs and RoPE rows (8 per load): per-lane addresses formed here.
+  struct FetchSP {
+    int kw;          // first key of this wave's rows
+    int idv;         // 512-wide: lane i < KR holds the page id of row i
+    uint64_t al[G::PAIR ? LK : 1];
+    uint64_t ar[RK];
+    uint32_t sbase;
+  };
+  auto prepare_sp = [&](int t, int u) __attribute__((always_inline)) {
+    FetchSP f;
+    f.kw = t0 + min(t, n_tiles - 1) * 64 + KR * wave;
+    f.sbase = ring_base + u * G::STAGE;
+    const int* ids = reinterpret_cast<const int*>(ring + PTAB + ((t % STAGES) * NW + wave) * 64);
+    if constexpr (G::PAIR) {
 #pragma unroll
-      for (int k = 0; k < LPW; ++k) issue_load(f, k);
+      for (int k = 0; k < LK; ++k) {
+        const int r = 2 * k + lrow;
+        const int key = min(f.kw + r, t_last);
+        f.al[k] = reinterpret_cast<uint64_t>(p.pool0) +
+                  (uint64_t)(((int64_t)ids[r] * p.page_stride +
+                              (int64_t)(key & pmask) * p.token_stride + head_off) * 2) +
+                  lunit * 16;
+      }
+      f.idv = 0;
     } else {
-      issue_clamped(f);
+      f.idv = ids[lane & (KR - 1)];
+      f.al[0] = 0;
+    }
+#pragma unroll
+    for (int k = 0; k < RK; ++k) {
+      const int r = 8 * k + rrow;
+      const int key = min(f.kw + r, t_last);
+      const int blk = wave * RK + k;
+      const int ru = (lane & 7) ^ ((4 * (blk & 1) + (lane >> 4)) & 7);
+      f.ar[k] = reinterpret_cast<uint64_t>(p.rope) +
+                (uint64_t)(((int64_t)ids[r] * p.rpage_stride +
+                            (int64_t)(key & pmask) * p.rtoken_stride) * 2) +
+                ru * 16;
+    }
+    return f;
+  };
+  auto issue_load_sp = [&](const FetchSP& f, int k) __attribute__((always_inline)) {
+    if (k < LK) {
+      const uint32_t dst = f.sbase + (wave * LK + k) * G::BSTR;
+      if constexpr (G::PAIR) {
+        dma16v(f.al[k], dst);
+      } else {
+        const int key = min(f.kw + k, t_last);
+        const int64_t id = __builtin_amdgcn_readlane(f.idv, k);
+        const char* base = uniform_ptr(
+            p.pool0 + (id * p.page_stride + (int64_t)(key & pmask) * p.token_stride + head_off) * 2);
+        dma16(base, vlat, dst);
+      }
+    } else {
+      const int kk = k - LK;
+      dma16v(f.ar[kk], f.sbase + G::R_OFF + (wave * RK + kk) * 1024);
+    }
+  };
+
+  auto issue = [&](int t, int u) __attribute__((always_inline)) {
+    if constexpr (SP) {
+      const FetchSP f = prepare_sp(t, u);
+      issue_ids(t + STAGES - 1);
+#pragma unroll
+      for (int k = 0; k < LPW; ++k) issue_load_sp(f, k);
+    } else {
+      const Fetch f = prepare(t, u);
+      if (f.valid == 64) {
+#pragma unroll
+        for (int k = 0; k < LPW; ++k) issue_load(f, k);
+      } else {
+        issue_clamped(f);
+      }
     }
   };
 
@@ -304,7 +395,8 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
   auto tile = [&](int t, auto ucst) __attribute__((always_inline)) {
     const int U = static_cast<int>(ucst);
     {
-      constexpr int ahead = (STAGES - 2) * LPW;
+      // loads per tile and wave: LPW cache loads (+ one page-id load)
+      constexpr int ahead = (STAGES - 2) * (LPW + (SP ? 1 : 0));
       __builtin_amdgcn_s_waitcnt((ahead & 15) | ((ahead >> 4) << 14) | (0x7 << 4) | (0xf << 8));
     }
     // every wave's loads of tile t have landed, and every wave is done with
@@ -312,9 +404,20 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
     __syncthreads();
     // refill the stage of tile t - 1 with tile t + STAGES - 1: a full tile's
     // loads are spread over the score MFMAs below, a partial one's issued now
-    const Fetch nf = prepare(t + STAGES - 1, (U + STAGES - 1) % STAGES);
-    const bool spread = nf.valid == 64;
-    if (!spread) issue_clamped(nf);
+    // (small pages: always spread, after the page ids of tile t + 2 STAGES - 2)
+    const auto nf = [&]() __attribute__((always_inline)) {
+      if constexpr (SP)
+        return prepare_sp(t + STAGES - 1, (U + STAGES - 1) % STAGES);
+      else
+        return prepare(t + STAGES - 1, (U + STAGES - 1) % STAGES);
+    }();
+    bool spread = true;
+    if constexpr (SP) {
+      issue_ids(t + 2 * STAGES - 2);
+    } else {
+      spread = nf.valid == 64;
+      if (!spread) issue_clamped(nf);
+    }
     const char* sb = ring + U * G::STAGE;
     const int key0 = t0 + t * 64;
 
@@ -352,7 +455,12 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
           sa[rt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[st % KD], qreg[rt][c], sa[rt][mt],
                                                                0, 0, 0);
         if (st + KD < NS) kb[st % KD] = kread(st + KD);
-        if ((st & 1) && (st >> 1) < LPW && spread) issue_load(nf, st >> 1);
+        if ((st & 1) && (st >> 1) < LPW && spread) {
+          if constexpr (SP)
+            issue_load_sp(nf, st >> 1);
+          else
+            issue_load(nf, st >> 1);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -513,7 +621,9 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
   // ---- workgroup-wide restart decision and the pair's row sums
   int* const flag = reinterpret_cast<int*>(ring);
   float* const lx = reinterpret_cast<float*>(ring + 256);
-  if (!RESCALE && lane == 0) flag[wave] = __builtin_amdgcn_ballot_w64(over) != 0 ? 1 : 0;
+  // the vote over all lanes of the wave, taken before a single lane stores it
+  const bool wave_over = __builtin_amdgcn_ballot_w64(over) != 0;
+  if (!RESCALE && lane == 0) flag[wave] = wave_over ? 1 : 0;
   float lsum[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
@@ -579,12 +689,12 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
 // RESCALE = false: the fixed-reference pass; records per workgroup whether
 // it had to give up (flags[block]).  RESCALE = true: the fix-up pass, a
 // second launch over the same grid that only works where the flag is set.
-template <int DC, int DR, int RT, int STAGES, int KQ, bool RESCALE>
+template <int DC, int DR, int RT, int STAGES, int KQ, bool RESCALE, bool SP>
 __global__ __launch_bounds__(2 * KQ * 64) __attribute__((amdgpu_waves_per_eu(KQ / 2, KQ / 2)))
 void decode_wide(Params p) {
   using G = Geo<DC, DR>;
   static_assert(STAGES * G::STAGE + 4 * RT * 1024 + PT_MAX * 4 <= 160 * 1024, "LDS");
-  static_assert((STAGES - 2) * (G::LOADS / (2 * KQ)) <= 63, "vmcnt range");
+  static_assert((STAGES - 2) * (G::LOADS / (2 * KQ) + 1) <= 63, "vmcnt range");
   static_assert(STAGES == 2 || STAGES == 3, "tile loop unrolled for 2 or 3 stages");
   __shared__ __attribute__((aligned(1024))) char ring[STAGES * G::STAGE + 4 * RT * 1024 + PT_MAX * 4];
 
@@ -621,7 +731,7 @@ void decode_wide(Params p) {
   itm.t_end = min(itm.t0 + chunk, itm.L);
   itm.n_tiles = (itm.t_end - itm.t0 + 63) / 64;
 
-  const bool gave_up = stream<DC, DR, RT, STAGES, KQ, RESCALE>(p, itm, ring);
+  const bool gave_up = stream<DC, DR, RT, STAGES, KQ, RESCALE, SP>(p, itm, ring);
   if constexpr (!RESCALE) {
     if (threadIdx.x == 0) p.flags[blockIdx.x] = gave_up ? 1 : 0;
   }
@@ -629,17 +739,17 @@ void decode_wide(Params p) {
 
 }  // namespace wide
 
-template <int DC, int DR, int RT, int S, int KQ>
+template <int DC, int DR, int RT, int S, int KQ, bool SP>
 int launch_wide_one(Params p, int n_items, hipStream_t stream) {
   p.n_items = n_items;
   p.row_blocks = (p.rows + 32 * RT - 1) / (32 * RT);
   const int n_groups = p.h_q / p.g;
   const int units = (n_items + n_groups - 1) / n_groups;   // (sequence, chunk) pairs
   const dim3 grid((units + 7) / 8 * 8 * n_groups * p.row_blocks);
-  hipLaunchKernelGGL((wide::decode_wide<DC, DR, RT, S, KQ, false>), grid, dim3(2 * KQ * 64), 0,
+  hipLaunchKernelGGL((wide::decode_wide<DC, DR, RT, S, KQ, false, SP>), grid, dim3(2 * KQ * 64), 0,
                      stream, p);
   // fix-up pass: exits at once unless the first pass flagged the workgroup
-  hipLaunchKernelGGL((wide::decode_wide<DC, DR, RT, S, KQ, true>), grid, dim3(2 * KQ * 64), 0,
+  hipLaunchKernelGGL((wide::decode_wide<DC, DR, RT, S, KQ, true, SP>), grid, dim3(2 * KQ * 64), 0,
                      stream, p);
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
@@ -650,12 +760,19 @@ int launch_wide_one(Params p, int n_items, hipStream_t stream) {
 // each tile's keys four ways over eight waves (two per SIMD, so one wave's
 // softmax and waits overlap another's MFMAs); 512-wide latents need the
 // register budget of one wave per SIMD and split keys two ways.
-template <int DC, int DR>
-int launch_wide(const Params& p, int n_items, hipStream_t stream) {
+template <int DC, int DR, bool SP>
+int launch_wide_sp(const Params& p, int n_items, hipStream_t stream) {
   constexpr int S = (DC >= 512) ? 2 : 3;
   constexpr int KQ = (DC >= 512) ? 2 : WIDE_KQ256;
-  if (p.rows <= 32) return launch_wide_one<DC, DR, 1, S, KQ>(p, n_items, stream);
-  return launch_wide_one<DC, DR, 2, S, KQ>(p, n_items, stream);
+  if (p.rows <= 32) return launch_wide_one<DC, DR, 1, S, KQ, SP>(p, n_items, stream);
+  return launch_wide_one<DC, DR, 2, S, KQ, SP>(p, n_items, stream);
+}
+
+// pages of fewer than 64 tokens: per-row page ids
+template <int DC, int DR>
+int launch_wide(const Params& p, int n_items, hipStream_t stream) {
+  return p.page_shift < 6 ? launch_wide_sp<DC, DR, true>(p, n_items, stream)
+                          : launch_wide_sp<DC, DR, false>(p, n_items, stream);
 }
 
 }  // namespace

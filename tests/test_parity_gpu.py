@@ -71,11 +71,43 @@ def test_nan_sentinels_in_unused_slots(name):
     _check(w, inp, f"{name}/nan", chunk_tokens=128)
 
 
-@pytest.mark.parametrize("page_size", [1, 16, 256])
-def test_page_sizes(page_size):
-    w = SMALL["gla2"].with_(page_size=page_size, max_seqlen=768)
-    print(f"[page] {page_size}", flush=True)
-    _check(w, synth.make_inputs(w), f"P{page_size}")
+def _head_major(d):
+    """The same logical pools over head-major storage [pages][heads][page][width]."""
+    for k in ("pool0", "pool1", "rope"):
+        if d[k] is not None:
+            d[k] = d[k].permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+    return d
+
+
+# every power-of-two page size: single-token and other pages smaller than a
+# 16-key slice (per-row page ids), pages of 16..32 tokens (one id per slice
+# in the GQA/GTA kernel, per-row ids in the latent one), and whole tiles
+PAGE_NAMES = ["gqa_llama8b", "gqa_d64_mqa", "gta_8k", "gta_causal2", "mla", "gla2", "gla2_spec4",
+              "gla2_h32"]
+
+
+@pytest.mark.parametrize("name", PAGE_NAMES)
+@pytest.mark.parametrize("page_size", [1, 2, 4, 8, 16, 32, 128, 256])
+def test_page_sizes(name, page_size):
+    w = SMALL[name].with_(page_size=page_size)
+    chunk = 192 if page_size in (2, 32) else 0
+    print(f"[page] {name} P={page_size} chunk={chunk}", flush=True)
+    _check(w, synth.make_inputs(w), f"{name}/P{page_size}", chunk_tokens=chunk)
+
+
+@pytest.mark.parametrize("name", ["gqa_llama8b", "gta_8k", "mla", "gla2_spec4"])
+@pytest.mark.parametrize("page_size", [1, 4, 16])
+def test_small_pages_head_major_and_nan_tails(name, page_size):
+    """Head-major pools (other strides) and NaN in every unused page slot
+    and unreferenced page."""
+    w = SMALL[name].with_(page_size=page_size)
+    print(f"[page-hnd] {name} P={page_size}", flush=True)
+    inp = synth.make_inputs(w, tail_fill=np.nan, extra_pages=5)
+    d = _head_major(H.to_device(w, inp))
+    out, lse, _ = H.run(w, d, chunk_tokens=128)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.decode(w, inp)
+    H.compare(H.to_np(out), H.to_np(lse), ref, ref_lse, H.value_max(w, inp), f"{name}/hnd/P{page_size}")
 
 
 def test_empty_and_single_token_sequences():
@@ -166,14 +198,67 @@ def test_gather_probe_recovers_physical_rows():
         assert np.all(np.rint(o[b, 0, 0]) == pg * 1000 + tgt % w.page_size)
 
 
+def _probe_codes(pg, sl):
+    """Exact bf16 integers (< 256) that name a physical row."""
+    return np.array([pg % 256, pg // 256, sl % 256, 7.0])
+
+
+@pytest.mark.parametrize("kind", ["gqa", "gta", "mla", "gla2"])
+@pytest.mark.parametrize("page_size", [1, 4, 16, 64])
+def test_gather_probe_streaming_kernels(kind, page_size):
+    """bf16 streaming kernels: values encode their own physical (page, slot)
+    as exact integers and one key per sequence dominates its query by 128
+    (natural log units: every other weight underflows to exactly zero), so
+    the output must name exactly that row."""
+    base = {"gqa": "gqa_llama8b", "gta": "gta_8k", "mla": "mla", "gla2": "gla2"}[kind]
+    w = SMALL[base].with_(batch=3, seqlen_lo=300, seqlen_hi=700, max_seqlen=768,
+                          page_size=page_size, q_std=0.0)
+    inp = synth.make_inputs(w)
+    p0 = np.zeros_like(inp["pool0"])
+    p1 = None if inp["pool1"] is None else np.zeros_like(inp["pool1"])
+    rp = None if inp["rope"] is None else np.zeros_like(inp["rope"])
+    vals = p1 if kind == "gqa" else p0   # the values the call attends over
+    for pg in range(p0.shape[0]):
+        for sl in range(w.page_size):
+            vals[pg, sl, :, :4] = _probe_codes(pg, sl)
+    L = inp["seqlens"]
+    targets = [int(L[0]) - 1, 3, int(L[2]) // 2]
+    q = np.zeros_like(inp["q"])
+    for b, tgt in enumerate(targets):
+        pg = inp["page_table"][b, tgt // w.page_size]
+        sl = tgt % w.page_size
+        if kind == "gqa":
+            p0[pg, sl, :, 5] = 1.0
+            q[b, :, :, 5] = 128.0
+        elif kind == "gta":
+            # the key's non-RoPE half is the tied row's first half
+            p0[pg, sl, :, 5] = 1.0
+            q[b, :, :, 5] = 128.0
+        else:
+            rp[pg, sl, 0, 0] = 1.0        # pre-rotated RoPE key
+            q[b, :, :, w.head_dim] = 128.0
+    inp.update(pool0=p0, pool1=p1, rope=rp, q=q)
+    w = w.with_(softmax_scale=1.0)
+    out, _, _ = H.run(w, H.to_device(w, inp), chunk_tokens=128)
+    torch.cuda.synchronize()
+    o = out.float().cpu().numpy()
+    for b, tgt in enumerate(targets):
+        pg = int(inp["page_table"][b, tgt // w.page_size])
+        want = _probe_codes(pg, tgt % w.page_size)
+        got = o[b, :, :, :4].reshape(-1, 4)
+        assert np.all(got == want), f"{kind} P={page_size} seq {b}: {got[0]} != {want}"
+
+
 # ------------------------------------------------------------ full size
-FULL = ["gqa_fp32_tiny", "gqa_llama8b", "gta_8k", "mla", "gla2", "gla2_spec4_128k"]
+FULL = ["gqa_fp32_tiny", "gqa_llama8b", "gta_8k", "mla", "gla2", "gla2_spec4_128k",
+        "gqa_llama8b@P1", "gla2@P1"]
 
 
 @pytest.mark.slow
 @pytest.mark.parametrize("name", FULL)
 def test_full_size_sampled(name):
-    w = W[name]
+    base, _, pg = name.partition("@P")
+    w = W[base] if not pg else W[base].with_(page_size=int(pg))
     print(f"[full] {name}", flush=True)
     inp = synth.make_inputs(w)
     d = H.to_device(w, inp)
