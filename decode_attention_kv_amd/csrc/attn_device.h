@@ -203,7 +203,7 @@ __device__ __forceinline__ void arrive_and_merge(const Params& p, uint32_t* coun
 // They set the grid-dependent fields of a copy of `p` and enqueue on `stream`.
 // General kernel: every kind / dtype / width the entry points accept.
 int run_general(int kind, bool bf16, int w0, const Params& p, int n_items, hipStream_t stream);
-// Streaming GQA / GTA kernel (bf16, pages >= 64 tokens, <= 64 rows per group).
+// Streaming GQA / GTA kernel (bf16, any power-of-two page size, <= 64 rows per group).
 int run_narrow(int kind, int d, const Params& p, int n_items, int groups, int stages,
                hipStream_t stream);
 // Streaming latent kernel (bf16, pages >= 64 tokens, d_c 256 or 512, d_r 64).

@@ -12,6 +12,20 @@
 namespace attn_internal {
 
 constexpr int kTile = 64;          // keys per tile; chunks are multiples of it
+
+// Latent streaming kernel geometry: the waves of a workgroup split each
+// tile's keys KQ ways (2 KQ waves, two row halves), and each wave holds RT
+// tiles of 16 query rows, so a workgroup covers 32 RT rows of a group.
+#ifndef WIDE_KQ512
+#define WIDE_KQ512 2
+#endif
+#ifndef WIDE_KQ256
+#define WIDE_KQ256 4
+#endif
+constexpr int wide_kq(int d_c) { return d_c >= 512 ? WIDE_KQ512 : WIDE_KQ256; }
+constexpr int wide_rt(int d_c, int rows) {
+  return (rows <= 32 || (d_c >= 512 && WIDE_KQ512 > 2)) ? 1 : 2;
+}
 constexpr int kNarrowWaves = 4;    // waves per workgroup of the streaming kernel
 constexpr int kNarrowStageTarget = 65536;  // LDS bytes of the streaming ring
 
@@ -84,7 +98,8 @@ inline KernelChoice choose_kernel(const attn_shape_t& sh) {
   if (k.narrow && sh.kind == ATTN_KIND_LATENT) {
     k.stages = sh.head_dim >= 512 ? 2 : 3;
     k.wgs_per_cu = 1;
-    k.row_blocks = k.rows <= 32 ? 1 : (k.rows + 63) / 64;
+    const int wg_rows = 32 * wide_rt(sh.head_dim, k.rows);
+    k.row_blocks = (k.rows + wg_rows - 1) / wg_rows;
     k.same_xcd_groups = true;  // groups share RoPE rows, row blocks latent rows
     k.rmax = 1.25;
     k.fixed_tiles = 8.0;
@@ -116,14 +131,16 @@ inline KernelChoice choose_kernel(const attn_shape_t& sh) {
 // fp32 LSE_part [slots][q_len][h_q] (256-byte padded), then one int32 flag
 // per workgroup of the latent streaming kernel (its grid: the (sequence,
 // chunk) units padded to a multiple of 8, times groups, times at most
-// ceil(rows / 64) row blocks).
+// ceil(rows / 32) row blocks).
 inline size_t flags_offset(const attn_plan_t* plan, int h_q, int d_v) {
   const size_t rows = (size_t)plan->n_partial_slots * plan->q_len * h_q;
   return (rows * d_v * 4 + 255) / 256 * 256 + (rows * 4 + 255) / 256 * 256;
 }
+// An upper bound of the row blocks of any streaming kernel: blocks of at
+// least 32 rows (the plan does not record the latent width).
 inline int64_t row_blocks_of(const attn_plan_t* plan, int h_q) {
   const int64_t rows = (int64_t)(plan->n_groups > 0 ? h_q / plan->n_groups : 0) * plan->q_len;
-  return (rows + 63) / 64 > 0 ? (rows + 63) / 64 : 1;
+  return (rows + 31) / 32 > 0 ? (rows + 31) / 32 : 1;
 }
 inline size_t flags_bytes(const attn_plan_t* plan, int h_q) {
   // grid of the latent streaming kernel: (sequence, chunk) units padded to
@@ -134,7 +151,8 @@ inline size_t flags_bytes(const attn_plan_t* plan, int h_q) {
   return ((size_t)blocks * 4 + 255) / 256 * 256;
 }
 // Merge arrival counters (plan->counters): one per (sequence, group, block
-// of 64 rows), indexed (b * groups + j) * row_blocks + block.
+// of 32 rows), of which the kernels use (b * groups + j) * row_blocks + block
+// for their own row_blocks (blocks of 32 or 64 rows).
 inline size_t counter_count(const attn_plan_t* plan, int h_q) {
   return (size_t)plan->batch * plan->n_groups * row_blocks_of(plan, h_q);
 }

@@ -46,10 +46,8 @@
 // offsets are spread over the lanes, and no scalar or vector wait sits
 // between a page-table read and its use).
 #include "attn_device.h"
+#include "attn_kernels.h"
 
-#ifndef WIDE_KQ256
-#define WIDE_KQ256 4
-#endif
 #ifndef WIDE_KD512
 #define WIDE_KD512 6
 #endif
@@ -763,9 +761,14 @@ int launch_wide_one(Params p, int n_items, hipStream_t stream) {
 template <int DC, int DR, bool SP>
 int launch_wide_sp(const Params& p, int n_items, hipStream_t stream) {
   constexpr int S = (DC >= 512) ? 2 : 3;
-  constexpr int KQ = (DC >= 512) ? 2 : WIDE_KQ256;
-  if (p.rows <= 32) return launch_wide_one<DC, DR, 1, S, KQ, SP>(p, n_items, stream);
-  return launch_wide_one<DC, DR, 2, S, KQ, SP>(p, n_items, stream);
+  constexpr int KQ = attn_internal::wide_kq(DC);
+  if constexpr (attn_internal::wide_rt(DC, 64) == 1) {
+    return launch_wide_one<DC, DR, 1, S, KQ, SP>(p, n_items, stream);
+  } else {
+    if (attn_internal::wide_rt(DC, p.rows) == 1)
+      return launch_wide_one<DC, DR, 1, S, KQ, SP>(p, n_items, stream);
+    return launch_wide_one<DC, DR, 2, S, KQ, SP>(p, n_items, stream);
+  }
 }
 
 // pages of fewer than 64 tokens: per-row page ids

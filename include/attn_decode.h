@@ -126,7 +126,7 @@ typedef struct {
  *
  * counters: with a non-NULL device array of attn_decode_counter_count()
  * uint32 the streaming kernels merge split rows themselves (the last split
- * workgroup of each (sequence, group, block of 64 query rows) to finish
+ * workgroup of each (sequence, group, block of 32 query rows) to finish
  * merges them, counted with atomic counters that wrap back to zero), so no
  * merge launch follows.  The array must hold zeros before its first use;
  * every complete call leaves it zero, so one array serves every later call

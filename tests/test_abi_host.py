@@ -144,7 +144,7 @@ def _ws_expect(plan, slots, h_q, d_v):
     rows = slots * plan.q_len * h_q
     pad = lambda x: (x + 255) // 256 * 256
     group_rows = h_q // plan.n_groups * plan.q_len
-    row_blocks = max(1, -(-group_rows // 64))
+    row_blocks = max(1, -(-group_rows // 32))
     units = -(-plan.n_items // plan.n_groups)
     flags = -(-units // 8) * 8 * plan.n_groups * row_blocks * 4
     return pad(rows * d_v * 4) + pad(rows * 4) + pad(flags)
@@ -166,14 +166,14 @@ def test_workspace_size():
 
 
 def test_counter_count():
-    # one merge counter per (sequence, group, block of 64 query rows)
+    # one merge counter per (sequence, group, block of 32 query rows)
     st, plan, _, _ = _plan([5000, 100, 7], groups=8, h_q=32)
     assert binding.attn_decode_counter_count(plan, 32) == 3 * 8 * 1
     st, plan, _, _ = _plan([4096] * 4, q_len=4, h_q=128, groups=2, kind="latent", d=256,
                            d_rope=64, causal=1)
-    assert binding.attn_decode_counter_count(plan, 128) == 4 * 2 * 4
+    assert binding.attn_decode_counter_count(plan, 128) == 4 * 2 * 8
     st, plan, _, _ = _plan([300] * 5, h_q=128, groups=1, kind="latent", d=512, d_rope=64)
-    assert binding.attn_decode_counter_count(plan, 128) == 5 * 1 * 2
+    assert binding.attn_decode_counter_count(plan, 128) == 5 * 1 * 4
     assert binding.attn_decode_counter_count(plan, 0) == 0
     assert plan.counters is None  # the planner leaves it to the caller
 

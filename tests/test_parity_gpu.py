@@ -42,6 +42,16 @@ SMALL = {
     "gla2_spec4": small("gla2_spec4_128k", batch=2, seqlen_lo=4, seqlen_hi=700, max_seqlen=704),
     "mla_spec4": small("mla_spec4_128k", batch=2, seqlen_lo=4, seqlen_hi=500, max_seqlen=512),
     "gla2_h32": small("gla2", batch=2, h_q=32, seqlen_lo=1, seqlen_hi=300, max_seqlen=320),
+    # sweep points: q_len up to 8, per-device shares of fewer heads
+    "gqa_q8": small("gqa_llama8b", batch=2, q_len=8, causal=True, seqlen_lo=8, seqlen_hi=400,
+                    max_seqlen=448),
+    "mla_q8": small("mla", batch=2, q_len=8, causal=True, seqlen_lo=8, seqlen_hi=300,
+                    max_seqlen=320),
+    "gla2_q2": small("gla2", batch=2, q_len=2, causal=True, seqlen_lo=2, seqlen_hi=500,
+                     max_seqlen=512),
+    "gla8_share": small("gla2", batch=3, h_q=16, groups=1, seqlen_lo=1, seqlen_hi=600,
+                        max_seqlen=640),
+    "mla_h16": small("mla", batch=2, h_q=16, seqlen_lo=1, seqlen_hi=400, max_seqlen=448),
 }
 
 
