@@ -1,9 +1,10 @@
 """Compile libattn_decode.so (gfx950) in-tree with hipcc.
 
 Sources: csrc/attn_host.cpp (host-only planning and checks),
-csrc/attn_decode.hip (entry points, merge kernel) and one translation unit
+csrc/attn_decode.hip (entry points, merge kernel), one translation unit
 per decode kernel family (attn_general.hip, attn_narrow.hip,
-attn_wide.hip), compiled in parallel.  Packed-fp32 VALU ops are disabled
+attn_wide.hip) and the cache append (attn_append.hip), compiled in
+parallel.  Packed-fp32 VALU ops are disabled
 for device code.
 """
 import concurrent.futures
@@ -17,7 +18,7 @@ LIB = os.path.join(PKG, "libattn_decode.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 SOURCES = ("attn_host.cpp", "attn_decode.hip", "attn_general.hip", "attn_narrow.hip",
-           "attn_wide.hip")
+           "attn_wide.hip", "attn_append.hip")
 
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-I" + os.path.join(ROOT, "include"),

@@ -99,6 +99,9 @@ def lib():
     L.attn_decode_merge.argtypes = [POINTER(Plan), c_int, c_int, c_int, c_void_p, c_size_t,
                                     c_void_p, c_void_p, c_void_p]
     L.attn_decode_merge.restype = c_int
+    L.attn_kv_append.argtypes = [POINTER(PagedKV), c_int, c_int, c_int, c_void_p, c_void_p, c_int,
+                                 c_void_p, c_float, c_void_p]
+    L.attn_kv_append.restype = c_int
     L.attn_paged_kv_check.argtypes = [POINTER(PagedKV)]
     L.attn_paged_kv_check.restype = c_int
     _lib = L
@@ -156,6 +159,12 @@ def attn_decode_latent(kv, q, out, lse, q_len, h_q, h_c, d_c, d_rope, scale, fla
 def attn_decode_merge(plan, h_q, d_v, dtype, ws, ws_bytes, out, lse, stream) -> int:
     return lib().attn_decode_merge(ctypes.byref(plan), h_q, d_v, dtype, ws, ws_bytes, out, lse,
                                    stream)
+
+
+def attn_kv_append(kv, q_len, heads, width, new0, new1, d_rope, new_rope, rope_theta,
+                   stream) -> int:
+    return lib().attn_kv_append(ctypes.byref(kv), q_len, heads, width, new0, new1, d_rope,
+                                new_rope, rope_theta, stream)
 
 
 def attn_paged_kv_check(kv: PagedKV) -> int:
@@ -277,6 +286,25 @@ def decode(kind: str, q, pool0, pool1, rope, page_table, seqlens, seqlens_host, 
     if st != ATTN_OK:
         raise AttnError(st, f"attn_decode_{kind}")
     return out, lse, plan, workspace
+
+
+def kv_append(pool0, pool1, rope, page_table, seqlens, new0, new1=None, new_rope=None,
+              rope_theta: float = 0.0, stream=None):
+    """Write a step's new rows (new0/new1 [B, q_len, heads, width], new_rope
+    [B, q_len, d_rope]) into the paged pools (attn_kv_append)."""
+    import torch
+
+    kv = paged_kv(pool0, pool1, rope, page_table, seqlens)
+    B, T, Hh, Wd = new0.shape
+    for t in (new0, new1, new_rope):
+        if t is not None and not t.is_contiguous():
+            raise ValueError("new rows must be contiguous")
+    d_rope = 0 if new_rope is None else new_rope.shape[-1]
+    s = (stream if stream is not None else torch.cuda.current_stream(new0.device)).cuda_stream
+    st = attn_kv_append(kv, T, Hh, Wd, new0.data_ptr(), _ptr(new1), d_rope, _ptr(new_rope),
+                        float(rope_theta), s)
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_kv_append")
 
 
 def merge(plan: DevicePlan, out, lse, workspace, stream=None):

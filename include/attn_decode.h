@@ -254,6 +254,32 @@ int attn_decode_merge(const attn_plan_t* plan, int h_q, int d_v, attn_dtype_t dt
                       hipStream_t stream);
 
 /*
+ * Paged KV append: write the rows of a step's new tokens into the cache
+ * before the decode call that reads them.  Sequence b's q_len new tokens
+ * take positions L_b - q_len .. L_b - 1 (kv->seqlens already counts them, as
+ * in the decode calls) and land in page page_table[b][pos / page_size],
+ * slot pos % page_size, through the descriptor's strides; the caller has
+ * already assigned those pages.  Positions below 0 are skipped.
+ *   new0      [batch][q_len][heads][width] rows for pool0 (GQA keys, GTA tied
+ *             state, latent rows), device, kv->dtype
+ *   new1      same shape for pool1 (GQA values) or NULL (pool1 untouched)
+ *   new_rope  [batch][q_len][d_rope] RoPE key rows for rope_pool, or NULL;
+ *             with rope_theta > 0 each is rotated at its position
+ *             (rotate-half pairs (k, k + d_rope/2), angle pos *
+ *             theta^(-2k/d_rope), computed in fp32) before it is stored:
+ *             latent caches hold rotated keys ("Hardware-Efficient Attention
+ *             for Fast Decoding", review page, Core claim), GTA caches raw
+ *             ones (pass rope_theta <= 0; the decode rotates them).
+ * Copies are exact; rotated keys are rounded to kv->dtype.  Row starts and
+ * row widths must be multiples of 16 bytes, d_rope even and at most 64.
+ * Returns ATTN_OK once enqueued on `stream`, INVALID_ARG (nothing enqueued)
+ * for inconsistent arguments.
+ */
+int attn_kv_append(const attn_paged_kv_t* kv, int q_len, int heads, int width, const void* new0,
+                   const void* new1, int d_rope, const void* new_rope, float rope_theta,
+                   hipStream_t stream);
+
+/*
  * Host-side consistency check of a descriptor whose page_table and seqlens
  * point to HOST copies: every page a sequence uses is in [0, num_pages) and
  * every length fits the page table.  Returns ATTN_OK or INVALID_ARG.

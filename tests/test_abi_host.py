@@ -273,3 +273,53 @@ def test_merge_validation():
     plan.items, plan.seqinfo = 0x10000, 0x20000
     # nothing split: a no-op that succeeds without touching the GPU
     assert M(plan, 32, 128, binding.ATTN_BF16, 0, 0, 0x700000, None, None) == binding.ATTN_OK
+
+
+def _append_kv():
+    kv = binding.PagedKV()
+    kv.pool0, kv.pool1, kv.rope_pool = 0x100000, 0x200000, 0x300000
+    kv.page_table, kv.seqlens = 0x400000, 0x500000
+    kv.batch, kv.max_pages_per_seq, kv.page_size, kv.num_pages = 2, 4, 64, 8
+    kv.page_stride, kv.token_stride, kv.head_stride = 64 * 8 * 128, 8 * 128, 128
+    kv.rope_page_stride, kv.rope_token_stride, kv.rope_head_stride = 64 * 64, 64, 0
+    kv.dtype = binding.ATTN_BF16
+    return kv
+
+
+@pytest.mark.parametrize("case", ["null_kv", "null_new0", "q_len0", "width_not_16B", "odd_rope",
+                                  "rope_too_wide", "rope_without_pool", "values_without_pool",
+                                  "page_not_pow2", "unaligned_new0", "neg_stride"])
+def test_append_rejects_bad_arguments(case):
+    """attn_kv_append validates on the host and enqueues nothing on error
+    (fake, never dereferenced device pointers)."""
+    kv = _append_kv()
+    args = dict(q_len=1, heads=8, width=128, new0=0x600000, new1=0x700000, d_rope=64,
+                new_rope=0x800000, theta=0.0)
+    if case == "null_kv":
+        assert binding.lib().attn_kv_append(None, 1, 8, 128, 0x600000, None, 0, None, 0.0,
+                                            None) == binding.ATTN_ERR_INVALID_ARG
+        return
+    if case == "null_new0":
+        args["new0"] = None
+    elif case == "q_len0":
+        args["q_len"] = 0
+    elif case == "width_not_16B":
+        args["width"] = 100
+    elif case == "odd_rope":
+        args["d_rope"] = 63
+    elif case == "rope_too_wide":
+        args["d_rope"] = 128
+    elif case == "rope_without_pool":
+        kv.rope_pool = None
+    elif case == "values_without_pool":
+        kv.pool1 = None
+    elif case == "page_not_pow2":
+        kv.page_size = 48
+    elif case == "unaligned_new0":
+        args["new0"] = 0x600008
+    elif case == "neg_stride":
+        kv.token_stride = -1024
+    st = binding.attn_kv_append(kv, args["q_len"], args["heads"], args["width"], args["new0"],
+                                args["new1"], args["d_rope"], args["new_rope"], args["theta"],
+                                None)
+    assert st == binding.ATTN_ERR_INVALID_ARG, case
