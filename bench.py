@@ -187,6 +187,9 @@ def main():
     ap.add_argument("--plan-mem", choices=["device", "host"], default="device",
                     help="device: copy each step's plan to HBM; host: kernels read it from "
                          "pinned host memory")
+    ap.add_argument("--with-append", action="store_true",
+                    help="each step first writes the q_len newest cache rows of every sequence "
+                         "(attn_kv_append, the same rows again) before planning and decoding")
     ap.add_argument("--set", action="append", default=[], metavar="FIELD=VALUE",
                     help="override a workload field (e.g. q_len=2, h_q=16, groups=1, "
                          "page_size=1, batch=64); the result is then not the named workload")
@@ -290,6 +293,27 @@ def main():
     stream = torch.cuda.current_stream(dev)
     s = stream.cuda_stream
 
+    if args.with_append:
+        # the newest q_len rows of every sequence, written back in place each step
+        T_new = w.q_len
+        rows = {}
+        for key, pool in (("new0", pool0), ("new1", pool1), ("rope", rope)):
+            if pool is None:
+                rows[key] = None
+                continue
+            t = torch.empty((B, T_new) + tuple(pool.shape[2:]), dtype=pool.dtype, device=dev)
+            for b in range(B):
+                for tt in range(T_new):
+                    pos = int(seqlens_host[b]) - T_new + tt
+                    if pos >= 0:
+                        t[b, tt] = pool[int(inp["page_table"][b, pos // w.page_size]),
+                                        pos % w.page_size]
+            rows[key] = t if key != "rope" else t[:, :, 0, :].contiguous()
+        app_args = (T_new, pool0.shape[2], pool0.shape[3], rows["new0"].data_ptr(),
+                    None if rows["new1"] is None else rows["new1"].data_ptr(),
+                    0 if rows["rope"] is None else w.d_rope,
+                    None if rows["rope"] is None else rows["rope"].data_ptr(), 0.0)
+
     def step(k, evs, inner):
         """One step: plan (host) + upload, decode (which merges split rows
         itself, or a merge launch after it).  evs = [start, before decode,
@@ -297,6 +321,10 @@ def main():
         (each recorded event costs the stream a few microseconds, so steps
         without them give the step time)."""
         evs[0].record(stream)
+        if args.with_append:
+            st = binding.attn_kv_append(kv, *app_args, s)
+            if st != binding.ATTN_OK:
+                raise binding.AttnError(st, "attn_kv_append")
         plan, slot = make_plan(k)
         if inner:
             evs[1].record(stream)
@@ -388,6 +416,7 @@ def main():
                        "mean_seqlen": float(seqlens_host.mean()), "page_size": w.page_size,
                        "kv_bytes_per_step": int(kvb), "gpus": 1, "layout": args.layout,
                        "cache_flush": args.flush, "plan_mem": args.plan_mem,
+                       "with_append": bool(args.with_append),
                        "merge": args.merge},
             "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
             "tokens_per_s": round(tokens / (ms * 1e-3), 1),

@@ -111,6 +111,8 @@ inline KernelChoice choose_kernel(const attn_shape_t& sh) {
     const int lds = k.stages * narrow_stage_bytes(sh.kind, sh.head_dim, sh.d_rope) + 2048;
     int w = 163840 / lds;
     k.wgs_per_cu = w < 1 ? 1 : w > 2 ? 2 : w;
+    // more than 32 rows (four row tiles per wave): one wave per SIMD
+    if (k.rows > 32) k.wgs_per_cu = 1;
     // GTA groups read the same RoPE key rows: keep them on one XCD's L2
     k.same_xcd_groups = sh.kind == ATTN_KIND_GTA;
     k.rmax = sh.kind == ATTN_KIND_GTA ? 1.5 : 3.0;

@@ -211,7 +211,11 @@ struct SliceDMA {
 };
 
 template <int KIND, int D, int DR, int RT, int STAGES, bool SP>
-__global__ __launch_bounds__(NW * 64) void decode_narrow(Params p) {
+// Two workgroups (two waves per SIMD) share a CU up to two row tiles per
+// wave: with two, the register budget is held to that (one row tile fits
+// without asking; four: one wave per SIMD).
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RT == 2 ? 2 : 1)))
+void decode_narrow(Params p) {
   using G = Geo<KIND, D, DR>;
   constexpr int DN = D - DR;          // key entries from the K / tied row
   constexpr int NKC = D / 32;         // 32-dim k-chunks of the score MFMA
