@@ -1,8 +1,9 @@
 #!/usr/bin/env python3
 """Benchmark of paged-KV decode attention on one MI355X.
 
-One step is the whole hot path over one batch: the host split plan, its
-upload, the split-KV decode kernel and the log-sum-exp merge kernel.  Inputs
+One step is the whole hot path over one batch: the host split plan (packed
+into the kernels' launch arguments when it fits, else uploaded), the
+split-KV decode kernel and the log-sum-exp merge kernel.  Inputs
 are seeded and synthetic and sit in HBM before timing starts.  Before every
 timed step a 1 GiB read evicts the caches (L2 and the 256 MB Infinity
 Cache) outside the timed interval, so every step reads its cache from HBM
@@ -184,9 +185,10 @@ def main():
     ap.add_argument("--merge", choices=["fused", "launch"], default="launch",
                     help="launch: a merge launch after the decode (faster here); fused: "
                          "the decode kernel merges split rows itself (plan counters)")
-    ap.add_argument("--plan-mem", choices=["device", "host"], default="device",
-                    help="device: copy each step's plan to HBM; host: kernels read it from "
-                         "pinned host memory")
+    ap.add_argument("--plan-mem", choices=["auto", "inline", "device", "host"], default="auto",
+                    help="inline: the plan travels in the kernels' launch arguments (no "
+                         "upload); device: copy each step's plan to HBM; host: kernels read "
+                         "it from pinned host memory; auto: inline when it fits, else device")
     ap.add_argument("--with-append", action="store_true",
                     help="each step first writes the q_len newest cache rows of every sequence "
                          "(attn_kv_append, the same rows again) before planning and decoding")
@@ -256,6 +258,7 @@ def main():
     released = [None, None]
     dev_buf = torch.zeros((B + max_items, 4), dtype=torch.int32, device=dev)
     counters = None  # merge counters (zero-filled once), sized from the first plan
+    placement = [None]  # where the last plan went: inline / device / host
 
     def make_plan(k):
         i = k % 2
@@ -267,14 +270,22 @@ def main():
         if st != binding.ATTN_OK:
             raise binding.AttnError(st, "attn_decode_plan")
         n = B + plan.n_items
-        if args.plan_mem == "host":
+        if args.plan_mem == "inline" or (args.plan_mem == "auto" and plan.inline_ok):
+            if not plan.inline_ok:
+                raise SystemExit("the plan does not fit the launch arguments")
+            # packed from the host arrays into the kernels' launch arguments
+            plan.seqinfo = plan.items = None
+            placement[0] = "inline"
+        elif args.plan_mem == "host":
             # pinned host memory is mapped into the device address space
             base = host_buf[i].data_ptr()
+            plan.seqinfo, plan.items = base, base + B * 16
+            placement[0] = "host"
         else:
             dev_buf[:n].copy_(host_buf[i][:n], non_blocking=True)
             base = dev_buf.data_ptr()
-        plan.seqinfo = base
-        plan.items = base + B * 16
+            plan.seqinfo, plan.items = base, base + B * 16
+            placement[0] = "device"
         if fused:
             nonlocal counters
             if counters is None:
@@ -415,7 +426,7 @@ def main():
                        "head_dim": w.head_dim, "d_rope": w.d_rope,
                        "mean_seqlen": float(seqlens_host.mean()), "page_size": w.page_size,
                        "kv_bytes_per_step": int(kvb), "gpus": 1, "layout": args.layout,
-                       "cache_flush": args.flush, "plan_mem": args.plan_mem,
+                       "cache_flush": args.flush, "plan_mem": placement[0],
                        "with_append": bool(args.with_append),
                        "merge": args.merge},
             "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),

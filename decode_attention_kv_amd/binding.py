@@ -55,7 +55,11 @@ def shape(kind: str, dtype: int, batch: int, q_len: int, h_q: int, groups: int, 
 class Plan(Structure):
     _fields_ = [("n_items", c_int32), ("batch", c_int32), ("n_groups", c_int32),
                 ("q_len", c_int32), ("max_splits", c_int32), ("n_partial_slots", c_int32),
-                ("items", c_void_p), ("seqinfo", c_void_p), ("counters", c_void_p)]
+                ("items", c_void_p), ("seqinfo", c_void_p), ("counters", c_void_p),
+                ("items_host", c_void_p), ("seqinfo_host", c_void_p), ("inline_ok", c_int32)]
+
+
+ATTN_PLAN_INLINE_MAX = 800
 
 
 class AttnError(RuntimeError):
@@ -208,7 +212,7 @@ class DevicePlan:
     """A host plan plus its device copy (keeps the device arrays alive)."""
 
     def __init__(self, shape_: Shape, seqlens_host, device, cu_count=256, chunk_tokens=0,
-                 fused_merge=False):
+                 fused_merge=False, inline=False):
         import torch
 
         seqlens_host = np.ascontiguousarray(seqlens_host, dtype=np.int32)
@@ -223,10 +227,18 @@ class DevicePlan:
                                     self.items_host, self.seqinfo_host, max_items)
         if st != ATTN_OK:
             raise AttnError(st, "attn_decode_plan")
-        self.items_dev = torch.from_numpy(self.items_host[:plan.n_items].copy()).to(device)
-        self.seqinfo_dev = torch.from_numpy(self.seqinfo_host).to(device)
-        plan.items = self.items_dev.data_ptr()
-        plan.seqinfo = self.seqinfo_dev.data_ptr()
+        if inline:
+            # the plan travels in the kernels' launch arguments (read from the
+            # host arrays this object keeps alive)
+            if not plan.inline_ok:
+                raise AttnError(ATTN_ERR_INVALID_ARG, "plan does not fit the launch arguments")
+            self.items_dev = self.seqinfo_dev = None
+            plan.items = plan.seqinfo = None
+        else:
+            self.items_dev = torch.from_numpy(self.items_host[:plan.n_items].copy()).to(device)
+            self.seqinfo_dev = torch.from_numpy(self.seqinfo_host).to(device)
+            plan.items = self.items_dev.data_ptr()
+            plan.seqinfo = self.seqinfo_dev.data_ptr()
         # optional merge counters, zero-filled once; with them the streaming
         # kernels merge split rows themselves (one launch instead of two)
         self.counters = None
@@ -240,7 +252,8 @@ class DevicePlan:
 def decode(kind: str, q, pool0, pool1, rope, page_table, seqlens, seqlens_host, *, groups: int,
            scale: float, causal: bool = False, rope_theta: float = 0.0, d_rope: int = 0,
            out=None, lse=None, chunk_tokens: int = 0, cu_count: int = 256, plan=None,
-           workspace=None, stream=None, defer_merge: bool = False, fused_merge: bool = False):
+           workspace=None, stream=None, defer_merge: bool = False, fused_merge: bool = False,
+           inline_plan: bool = False):
     """Run one decode through the native library on torch tensors.
 
     kind: "gqa" | "gta" | "latent".  q [B, T, H, Dq]; pools as in the header.
@@ -248,7 +261,8 @@ def decode(kind: str, q, pool0, pool1, rope, page_table, seqlens, seqlens_host, 
     With ``defer_merge`` the split partials stay in the workspace and the
     caller finishes with ``merge``.  With ``fused_merge`` a new plan carries
     merge counters and the decode kernel merges split rows itself; otherwise
-    the merge is a second launch on the stream.
+    the merge is a second launch on the stream.  With ``inline_plan`` a new
+    plan is passed in the kernels' launch arguments instead of device arrays.
     """
     import torch
 
@@ -259,7 +273,7 @@ def decode(kind: str, q, pool0, pool1, rope, page_table, seqlens, seqlens_host, 
         dtype = ATTN_BF16 if pool0.dtype == torch.bfloat16 else ATTN_FP32
         sh = shape(kind, dtype, B, T, H, groups, width, d_rope, pool0.shape[1], causal)
         plan = DevicePlan(sh, seqlens_host, q.device, cu_count=cu_count, chunk_tokens=chunk_tokens,
-                          fused_merge=fused_merge)
+                          fused_merge=fused_merge, inline=inline_plan)
     need = attn_decode_workspace_size(plan.plan, H, d_v)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)

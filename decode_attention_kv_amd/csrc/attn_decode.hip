@@ -17,17 +17,18 @@ namespace {
 // Merge the split partials of every sequence with n_splits > 1.
 // grid (ceil(q_len*h_q / rows_per_block), batch); DV/4 threads per row.
 template <typename T, int DV>
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ o_part,
-                                                       const float* __restrict__ lse_part,
-                                                       const int32_t* __restrict__ seqinfo,
-                                                       T* __restrict__ out, float* __restrict__ lse,
-                                                       int rows_total) {
+__global__ __launch_bounds__(256) void combine_kernel(Params p) {
   constexpr int TPR = DV / 4;
   constexpr int RPB = 256 / TPR;
+  const float* __restrict__ o_part = p.o_part;
+  const float* __restrict__ lse_part = p.lse_part;
+  T* __restrict__ out = static_cast<T*>(p.out);
+  float* __restrict__ lse = p.lse;
+  const int rows_total = p.q_len * p.h_q;
   const int b = blockIdx.y;
-  const int n = seqinfo[4 * b + 0];
+  int n, base, L_unused, chunk_unused;
+  seq_info(p, b, n, base, L_unused, chunk_unused);
   if (n <= 1) return;
-  const int base = seqinfo[4 * b + 1];
   const int row = blockIdx.x * RPB + threadIdx.x / TPR;
   if (row >= rows_total) return;
   const int c4 = (threadIdx.x % TPR) * 4;
@@ -58,6 +59,25 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 // host side
 bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
+// the plan's device arrays, or a plan to pass in the launch arguments
+bool plan_on_device(const attn_plan_t* plan) { return plan->items && plan->seqinfo; }
+bool plan_inline(const attn_plan_t* plan) {
+  return !plan->items && !plan->seqinfo && plan->inline_ok && plan->items_host &&
+         plan->seqinfo_host && plan->n_groups > 0 &&
+         4 * (int64_t)plan->batch + plan->n_items / plan->n_groups <= ATTN_PLAN_INLINE_MAX;
+}
+// compact copy of a host plan into the launch arguments
+void pack_inline(Params& p, const attn_plan_t* plan) {
+  p.plan_inline = 1;
+  p.inl_batch = plan->batch;
+  std::memcpy(p.inl, plan->seqinfo_host, sizeof(int32_t) * 4 * plan->batch);
+  const int g = plan->n_groups;
+  for (int c = 0; c < plan->n_items / g; ++c) {
+    const int32_t* it = plan->items_host + 4 * (int64_t)c * g;
+    p.inl[4 * plan->batch + c] = (int32_t)((uint32_t)it[0] | ((uint32_t)it[2] << 16));
+  }
+}
+
 int ilog2_pow2(int v) {
   if (v <= 0 || (v & (v - 1))) return -1;
   int s = 0;
@@ -77,7 +97,8 @@ int validate(const attn_paged_kv_t* kv, const void* q, const void* out, int q_le
   if (!kv->pool0 || !kv->page_table || !kv->seqlens) return ATTN_ERR_INVALID_ARG;
   if (need_pool1 && !kv->pool1) return ATTN_ERR_INVALID_ARG;
   if (need_rope && !kv->rope_pool) return ATTN_ERR_INVALID_ARG;
-  if (!plan->items || !plan->seqinfo || plan->n_items <= 0) return ATTN_ERR_INVALID_ARG;
+  if (plan->n_items <= 0) return ATTN_ERR_INVALID_ARG;
+  if (!plan_on_device(plan) && !plan_inline(plan)) return ATTN_ERR_INVALID_ARG;
   if (kv->batch <= 0 || kv->batch != plan->batch || plan->n_groups != groups ||
       plan->q_len != q_len)
     return ATTN_ERR_INVALID_ARG;
@@ -141,6 +162,7 @@ void fill_common(Params& p, const attn_paged_kv_t* kv, const void* q, void* out,
   p.lse = lse;
   p.items = plan->items;
   p.seqinfo = plan->seqinfo;
+  if (!plan_on_device(plan)) pack_inline(p, plan);
   p.q_len = q_len;
   p.h_q = h_q;
   p.g = h_q / groups;
@@ -156,8 +178,7 @@ int launch_combine(const Params& p, const attn_plan_t* plan, hipStream_t stream)
   constexpr int RPB = 256 / (DV / 4);
   const int rows_total = p.q_len * p.h_q;
   dim3 grid((rows_total + RPB - 1) / RPB, plan->batch);
-  hipLaunchKernelGGL((combine_kernel<T, DV>), grid, dim3(256), 0, stream, p.o_part, p.lse_part,
-                     p.seqinfo, static_cast<T*>(p.out), p.lse, rows_total);
+  hipLaunchKernelGGL((combine_kernel<T, DV>), grid, dim3(256), 0, stream, p);
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
@@ -278,8 +299,9 @@ int attn_decode_latent(const attn_paged_kv_t* kv, const void* q, void* out, floa
 
 int attn_decode_merge(const attn_plan_t* plan, int h_q, int d_v, attn_dtype_t dtype,
                       const void* ws, size_t ws_bytes, void* out, float* lse, hipStream_t stream) {
-  if (!plan || !out || !plan->seqinfo || h_q <= 0 || plan->q_len <= 0 || plan->batch <= 0)
+  if (!plan || !out || h_q <= 0 || plan->q_len <= 0 || plan->batch <= 0)
     return ATTN_ERR_INVALID_ARG;
+  if (!plan_on_device(plan) && !plan_inline(plan)) return ATTN_ERR_INVALID_ARG;
   if (dtype != ATTN_BF16 && dtype != ATTN_FP32) return ATTN_ERR_INVALID_ARG;
   if (d_v != 64 && d_v != 128 && d_v != 256 && d_v != 512) return ATTN_ERR_UNSUPPORTED;
   if (plan->n_partial_slots <= 0) return ATTN_OK;
@@ -291,6 +313,7 @@ int attn_decode_merge(const attn_plan_t* plan, int h_q, int d_v, attn_dtype_t dt
   p.out = out;
   p.lse = lse;
   p.seqinfo = plan->seqinfo;
+  if (!plan_on_device(plan)) pack_inline(p, plan);
   p.q_len = plan->q_len;
   p.h_q = h_q;
   set_partials(p, plan, ws, plan->q_len, h_q, d_v);

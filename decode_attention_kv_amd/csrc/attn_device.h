@@ -53,7 +53,47 @@ struct Params {
   // RoPE: revolutions per position of frequency k as hi + lo floats
   float rope_hi[kMaxRope / 2];
   float rope_lo[kMaxRope / 2];
+  // plan in the launch arguments (plan_inline = 1): inl[4 b .. 4 b + 3] =
+  // n_splits, partial slot base, L, chunk of sequence b; inl[4 inl_batch +
+  // c] = b | split << 16 of chunk c, whose groups are items c * groups + j
+  int32_t plan_inline;
+  int32_t inl_batch;
+  int32_t inl[ATTN_PLAN_INLINE_MAX];
 };
+
+// One work item of the plan, from device arrays or the launch arguments;
+// `item` is wave-uniform, and so are the fields.
+struct PlanItem {
+  int b, j, split, t0, n_splits, slot_base, L, chunk;
+};
+__device__ __forceinline__ void seq_info(const Params& p, int b, int& n_splits, int& slot_base,
+                                         int& L, int& chunk) {
+  const int32_t* si = p.plan_inline ? p.inl + 4 * b : p.seqinfo + 4 * b;
+  n_splits = __builtin_amdgcn_readfirstlane(si[0]);
+  slot_base = __builtin_amdgcn_readfirstlane(si[1]);
+  L = __builtin_amdgcn_readfirstlane(si[2]);
+  chunk = __builtin_amdgcn_readfirstlane(si[3]);
+}
+__device__ __forceinline__ PlanItem load_item(const Params& p, int item) {
+  PlanItem r;
+  if (p.plan_inline) {
+    const int n_groups = p.h_q / p.g;
+    const int c = item / n_groups;
+    const uint32_t e = (uint32_t)__builtin_amdgcn_readfirstlane(p.inl[4 * p.inl_batch + c]);
+    r.b = (int)(e & 0xffffu);
+    r.split = (int)(e >> 16);
+    r.j = item - c * n_groups;
+  } else {
+    const int32_t* it = p.items + 4 * item;
+    r.b = __builtin_amdgcn_readfirstlane(it[0]);
+    r.j = __builtin_amdgcn_readfirstlane(it[1]);
+    r.split = __builtin_amdgcn_readfirstlane(it[2]);
+    r.t0 = __builtin_amdgcn_readfirstlane(it[3]);
+  }
+  seq_info(p, r.b, r.n_splits, r.slot_base, r.L, r.chunk);
+  if (p.plan_inline) r.t0 = r.split * r.chunk;  // chunks of equal length
+  return r;
+}
 
 template <typename T> struct DT;
 template <> struct DT<__bf16> { static constexpr int EPC = 8; };   // elements per 16 B

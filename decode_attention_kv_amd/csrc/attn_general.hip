@@ -102,10 +102,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(Params p) {
   const int rblk = rem >> 3;
   const int item = grp8 * 8 + (rem & 7);
   if (item >= p.n_items) return;
-  const int32_t* it = p.items + 4 * item;
-  const int b = it[0], j = it[1], split = it[2], t0 = it[3];
-  const int32_t* si = p.seqinfo + 4 * b;
-  const int n_splits = si[0], slot_base = si[1], L = si[2], chunk = si[3];
+  const PlanItem pi = load_item(p, item);
+  const int b = pi.b, j = pi.j, split = pi.split, t0 = pi.t0;
+  const int n_splits = pi.n_splits, slot_base = pi.slot_base, L = pi.L, chunk = pi.chunk;
   const int t_end = min(t0 + chunk, L);
 
   // query rows owned by this lane (one per row tile)

@@ -254,16 +254,9 @@ void decode_narrow(Params p) {
   const int rem = bid - blk * 8 * gsz;
   const int item = (blk * 8 + (rem & 7)) * gsz + (rem >> 3);
   if (item >= p.n_items) return;
-  const int32_t* it = p.items + 4 * item;
-  const int b = __builtin_amdgcn_readfirstlane(it[0]);
-  const int j = __builtin_amdgcn_readfirstlane(it[1]);
-  const int split = __builtin_amdgcn_readfirstlane(it[2]);
-  const int t0 = __builtin_amdgcn_readfirstlane(it[3]);
-  const int32_t* si = p.seqinfo + 4 * b;
-  const int n_splits = __builtin_amdgcn_readfirstlane(si[0]);
-  const int slot_base = __builtin_amdgcn_readfirstlane(si[1]);
-  const int L = __builtin_amdgcn_readfirstlane(si[2]);
-  const int chunk = __builtin_amdgcn_readfirstlane(si[3]);
+  const PlanItem pi = load_item(p, item);
+  const int b = pi.b, j = pi.j, split = pi.split, t0 = pi.t0;
+  const int n_splits = pi.n_splits, slot_base = pi.slot_base, L = pi.L, chunk = pi.chunk;
   const int t_end = min(t0 + chunk, L);
   const int n_tiles = (t_end - t0 + KTILE - 1) / KTILE;
   const int t_last = t_end - 1;

@@ -716,16 +716,15 @@ void decode_wide(Params p) {
   itm.rblk = sub - jl * rb_count;
   const int item = unit * n_groups + jl;
   if (item >= p.n_items) return;
-  const int32_t* it = p.items + 4 * item;
-  itm.b = __builtin_amdgcn_readfirstlane(it[0]);
-  itm.j = __builtin_amdgcn_readfirstlane(it[1]);
-  itm.split = __builtin_amdgcn_readfirstlane(it[2]);
-  itm.t0 = __builtin_amdgcn_readfirstlane(it[3]);
-  const int32_t* si = p.seqinfo + 4 * itm.b;
-  itm.n_splits = __builtin_amdgcn_readfirstlane(si[0]);
-  itm.slot_base = __builtin_amdgcn_readfirstlane(si[1]);
-  itm.L = __builtin_amdgcn_readfirstlane(si[2]);
-  const int chunk = __builtin_amdgcn_readfirstlane(si[3]);
+  const PlanItem pi = load_item(p, item);
+  itm.b = pi.b;
+  itm.j = pi.j;
+  itm.split = pi.split;
+  itm.t0 = pi.t0;
+  itm.n_splits = pi.n_splits;
+  itm.slot_base = pi.slot_base;
+  itm.L = pi.L;
+  const int chunk = pi.chunk;
   itm.t_end = min(itm.t0 + chunk, itm.L);
   itm.n_tiles = (itm.t_end - itm.t0 + 63) / 64;
 

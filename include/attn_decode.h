@@ -144,7 +144,22 @@ typedef struct {
   const int32_t* items;    /* DEVICE copy of items_host                          */
   const int32_t* seqinfo;  /* DEVICE copy of seqinfo_host                        */
   uint32_t* counters;      /* DEVICE merge arrival counters or NULL (see below)  */
+  const int32_t* items_host;   /* the host arrays attn_decode_plan filled        */
+  const int32_t* seqinfo_host;
+  int32_t inline_ok;       /* 1: the plan fits the kernels' launch arguments     */
 } attn_plan_t;
+
+/*
+ * Launch-argument plans.  A plan needs 4 * batch + n_items / n_groups int32
+ * in compact form (the sequences' info and one entry per chunk); when that
+ * is at most ATTN_PLAN_INLINE_MAX (and batch and n_splits_b stay below
+ * 65536), attn_decode_plan sets inline_ok.  A decode or merge call whose
+ * plan then has items == NULL and seqinfo == NULL packs the plan from
+ * items_host / seqinfo_host (which must still hold what attn_decode_plan
+ * wrote) into the kernels' launch arguments, so no upload is needed.  With
+ * items and seqinfo NULL and inline_ok 0 the calls return INVALID_ARG.
+ */
+#define ATTN_PLAN_INLINE_MAX 800
 
 /*
  * Shape of a decode call, as the planner needs it.

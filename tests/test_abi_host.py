@@ -208,6 +208,8 @@ def _fake_call(kind="gqa", **over):
     validation must reject it before any launch."""
     st, plan, _, _ = _plan([100, 200], groups=over.pop("plan_groups", 8), chunk=64)
     plan.items, plan.seqinfo = 0x10000, 0x20000
+    for k, v in over.pop("plan_fields", {}).items():
+        setattr(plan, k, v)
     kv = binding.PagedKV()
     kv.pool0, kv.pool1, kv.rope_pool = 0x100000, 0x200000, 0x300000
     kv.page_table, kv.seqlens = 0x400000, 0x500000
@@ -323,3 +325,25 @@ def test_append_rejects_bad_arguments(case):
                                 args["new1"], args["d_rope"], args["new_rope"], args["theta"],
                                 None)
     assert st == binding.ATTN_ERR_INVALID_ARG, case
+
+
+def test_launch_argument_plan_capacity():
+    # 4 * batch + chunks int32 must fit ATTN_PLAN_INLINE_MAX
+    st, plan, items, info = _plan([5000, 100, 7], groups=8, h_q=32)
+    chunks = plan.n_items // plan.n_groups
+    assert plan.inline_ok == 1 and 4 * 3 + chunks <= binding.ATTN_PLAN_INLINE_MAX
+    assert plan.items_host and plan.seqinfo_host
+    st, plan, _, _ = _plan([8192] * 200, groups=8, h_q=32)      # 800 + chunks > 800
+    assert plan.inline_ok == 0
+
+
+@pytest.mark.parametrize("kind", ["gqa", "gta", "latent"])
+def test_plan_without_device_arrays_needs_inline_ok(kind):
+    """Decode calls reject a plan with neither device arrays nor a fitting
+    launch-argument form, or with one device array only (fake, never
+    dereferenced device pointers)."""
+    d = dict(gqa=128, gta=128, latent=256)[kind]
+    extra = dict(d=d) if kind != "latent" else dict(d=d, plan_groups=2, groups=2)
+    for fields in (dict(items=None, seqinfo=None, inline_ok=0), dict(seqinfo=None),
+                   dict(items=None, seqinfo=None, items_host=None)):
+        assert _fake_call(kind, plan_fields=fields, **extra) == binding.ATTN_ERR_INVALID_ARG, fields

@@ -342,3 +342,31 @@ def test_fused_merge_counters_return_to_zero(name):
         H.compare(H.to_np(out), H.to_np(lse), ref, ref_lse, vmax, f"{name}/fused{chunk}")
         assert torch.equal(out, sep) and torch.equal(lse, sep_lse)
         assert int(counters.count_nonzero()) == 0
+
+
+@pytest.mark.parametrize("name", ["gqa_llama8b", "gta_causal2", "mla", "gla2_spec4",
+                                  "gqa_fp32_d128", "gqa_mha", "gla8_share"])
+@pytest.mark.parametrize("page_size", [1, 64])
+def test_launch_argument_plan_matches_device_plan(name, page_size):
+    """A plan passed in the kernels' launch arguments (no device copy) gives
+    bit-identical results, for the decode call and for a deferred merge."""
+    w = SMALL[name].with_(page_size=page_size) if w_pages_ok(name) else SMALL[name]
+    print(f"[inline] {name} P={w.page_size}", flush=True)
+    d = H.to_device(w, synth.make_inputs(w))
+    o1, l1, _ = H.run(w, d, chunk_tokens=128)
+    o2, l2, plan2 = H.run(w, d, chunk_tokens=128, inline_plan=True)
+    assert plan2.plan.items is None and plan2.plan.seqinfo is None
+    o3, l3, plan3, ws = binding.decode(
+        w.kind, d["q"], d["pool0"], d["pool1"], d["rope"], d["page_table"], d["seqlens"],
+        d["seqlens_host"], groups=w.groups, scale=w.softmax_scale, causal=w.causal,
+        rope_theta=w.rope_theta, d_rope=w.d_rope, chunk_tokens=128, defer_merge=True,
+        inline_plan=True)
+    binding.merge(plan3, o3, l3, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.equal(o1, o3) and torch.equal(l1, l3)
+
+
+def w_pages_ok(name):
+    # fp32 shapes run on the general kernel at their own page size
+    return SMALL[name].dtype == "bf16"
