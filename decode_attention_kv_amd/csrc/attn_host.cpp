@@ -16,21 +16,33 @@ using attn_internal::kTile;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Items of a plan with chunks of `ct` tiles, in launch order: full chunks
-// first (all of equal length), then the shorter tails, longest first, so
-// that the dispatcher's in-order list scheduling ends with the short ones.
-// Each entry is (sequence, split, tiles); groups are expanded by the caller.
+// Items of a plan with chunks of at most `ct` tiles, in launch order: full
+// chunks first, then the shorter ones, longest first, so that the
+// dispatcher's in-order list scheduling ends with the short ones.  With
+// `balanced` a sequence split n = ceil(tiles / ct) ways gets n chunks of
+// equal length (the last one shorter by the remainder).  Each entry is
+// (sequence, split, tiles); groups are expanded by the caller.
 struct Chunk {
   int32_t b, s, tiles;
 };
-void chunks_in_order(const std::vector<int64_t>& tiles, int64_t ct, std::vector<Chunk>* out) {
+// chunk length (tiles) of a sequence of `t` tiles under a plan of `ct`:
+// ct itself, or with balanced splits the same number of chunks made equal
+int64_t seq_chunk(int64_t t, int64_t ct, bool balanced) {
+  if (!balanced) return ct;
+  const int64_t n = std::max<int64_t>(1, ceil_div(t, ct));
+  return std::max<int64_t>(1, ceil_div(t, n));
+}
+void chunks_in_order(const std::vector<int64_t>& tiles, int64_t ct, std::vector<Chunk>* out,
+                     bool balanced) {
   out->clear();
   std::vector<Chunk> tails;
   const int batch = (int)tiles.size();
   for (int b = 0; b < batch; ++b) {
     const int64_t n = std::max<int64_t>(1, ceil_div(tiles[b], ct));
+    const int64_t cb = seq_chunk(tiles[b], ct, balanced);
     for (int64_t s = 0; s < n; ++s) {
-      const int64_t len = std::min<int64_t>(ct, tiles[b] - s * ct);
+      const int64_t len = std::min<int64_t>(cb, tiles[b] - s * cb);
+      if (len <= 0 && s > 0) break;  // (an empty sequence keeps its one item)
       (len == ct ? *out : tails).push_back({b, (int32_t)s, (int32_t)len});
     }
   }
@@ -137,6 +149,10 @@ int attn_decode_plan(const attn_shape_t* shape, const int32_t* seqlens_host, int
 
   int64_t ct;  // chunk length in tiles
   std::vector<Chunk> chunks;
+  // automatic plans split each sequence into chunks of equal length (one
+  // long chunk beside a short tail would set the kernel's end); a forced
+  // chunk length is used as given
+  const bool balanced = chunk_tokens == 0;
   chunks.reserve(1024);
   if (chunk_tokens > 0) {
     ct = chunk_tokens / kTile;
@@ -156,7 +172,7 @@ int attn_decode_plan(const attn_shape_t* shape, const int32_t* seqlens_host, int
       const int64_t c = ceil_div(max_tiles, n);
       *c_out = c;
       if (c < std::min<int64_t>(4, max_tiles)) return -1.0;  // chunks of >= 256 keys
-      chunks_in_order(tiles, c, &chunks);
+      chunks_in_order(tiles, c, &chunks, balanced);
       const int64_t wgs = (int64_t)chunks.size() * n_groups;
       if (wgs > max_items) return -1.0;
       if (n > 1 && wgs > 6 * 8 * (int64_t)slots) return -1.0;  // far finer than the GPU
@@ -194,7 +210,7 @@ int attn_decode_plan(const attn_shape_t* shape, const int32_t* seqlens_host, int
     if (n0 > 0) consider(n0 * 3 / 2);
     if (best_n == 0) ct = max_tiles;
   }
-  chunks_in_order(tiles, ct, &chunks);
+  chunks_in_order(tiles, ct, &chunks, balanced);
 
   // items in launch order, groups of one chunk consecutive
   const int64_t n_items = (int64_t)chunks.size() * n_groups;
@@ -210,7 +226,7 @@ int attn_decode_plan(const attn_shape_t* shape, const int32_t* seqlens_host, int
     seqinfo_host[4 * b + 0] = (int32_t)n;
     seqinfo_host[4 * b + 1] = (int32_t)(n > 1 ? slot : -1);
     seqinfo_host[4 * b + 2] = seqlens_host[b];
-    seqinfo_host[4 * b + 3] = chunk;
+    seqinfo_host[4 * b + 3] = (int32_t)(seq_chunk(tiles[b], ct, balanced) * kTile);
     if (n > 1) slot += n;
   }
   int64_t k = 0;
@@ -219,7 +235,7 @@ int attn_decode_plan(const attn_shape_t* shape, const int32_t* seqlens_host, int
       items_host[4 * k + 0] = c.b;
       items_host[4 * k + 1] = j;
       items_host[4 * k + 2] = c.s;
-      items_host[4 * k + 3] = (int32_t)((int64_t)c.s * chunk);
+      items_host[4 * k + 3] = (int32_t)((int64_t)c.s * seq_chunk(tiles[c.b], ct, balanced) * kTile);
       ++k;
     }
   }

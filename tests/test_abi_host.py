@@ -86,10 +86,13 @@ def test_plan_is_deterministic_and_longest_first():
     assert np.array_equal(a[2], b[2]) and np.array_equal(a[3], b[3])
     items, info = a[2], a[3]
     lens = [min(t0 + info[b_, 3], info[b_, 2]) - t0 for b_, _, _, t0 in items.tolist()]
-    full = [l == info[b_, 3] for (b_, _, _, _), l in zip(items.tolist(), lens)]
-    # all full-length chunks come before any shorter tail chunk, and the
-    # tails follow longest first
-    assert full == sorted(full, reverse=True)
+    # chunks in launch order, longest first
+    assert lens == sorted(lens, reverse=True)
+    # a forced chunk length: full chunks first, then the tails longest first
+    items, info = _plan(seqlens, chunk=1024)[2:]
+    lens = [min(t0 + 1024, info[b_, 2]) - t0 for b_, _, _, t0 in items.tolist()]
+    full = [l == 1024 for l in lens]
+    assert (info[:, 3] == 1024).all() and full == sorted(full, reverse=True)
     tails = [l for l, f in zip(lens, full) if not f]
     assert tails == sorted(tails, reverse=True)
 
@@ -104,7 +107,17 @@ def test_plan_large_batches(batch, groups, kind):
     st, plan, items, info = _plan(seqlens, h_q=h_q, groups=groups, kind=kind, d=d,
                                   d_rope=d_rope)
     assert st == 0 and plan.n_items == len(items) >= batch * groups
-    assert info[:, 3].min() == info[:, 3].max() and info[0, 3] % 64 == 0
+    _assert_balanced(info)
+
+
+def _assert_balanced(info):
+    """Automatic plans: a sequence split n ways has n chunks of equal length
+    (whole 64-token tiles) of which only the last is shorter."""
+    for n, _, L, ch in info.tolist():
+        assert ch % 64 == 0 and ch > 0
+        tiles = -(-L // 64)
+        if n > 1:
+            assert ch == -(-tiles // n) * 64 and (n - 1) * ch < L <= n * ch
 
 
 def test_plan_auto_split_balances_load():
@@ -113,6 +126,7 @@ def test_plan_auto_split_balances_load():
     st, plan, items, info = _plan(seqlens, q_len=4, h_q=128, groups=2, kind="latent", d=256,
                                   d_rope=64, causal=1)
     assert st == 0 and plan.max_splits > 1
+    _assert_balanced(info)
     # partial traffic stays a small fraction of the cache bytes
     part = plan.n_partial_slots * 4 * 128 * (256 + 1) * 4 * 2
     kv = int(seqlens.sum()) * 1152
