@@ -192,6 +192,8 @@ def main():
     ap.add_argument("--with-append", action="store_true",
                     help="each step first writes the q_len newest cache rows of every sequence "
                          "(attn_kv_append, the same rows again) before planning and decoding")
+    ap.add_argument("--queue", choices=["on", "off"], default="off",
+                    help="on: the GQA kernel hands items out through a work-queue counter")
     ap.add_argument("--set", action="append", default=[], metavar="FIELD=VALUE",
                     help="override a workload field (e.g. q_len=2, h_q=16, groups=1, "
                          "page_size=1, batch=64); the result is then not the named workload")
@@ -259,6 +261,7 @@ def main():
     dev_buf = torch.zeros((B + max_items, 4), dtype=torch.int32, device=dev)
     counters = None  # merge counters (zero-filled once), sized from the first plan
     placement = [None]  # where the last plan went: inline / device / host
+    queue = torch.zeros(1, dtype=torch.int32, device=dev) if args.queue == "on" else None
 
     def make_plan(k):
         i = k % 2
@@ -286,6 +289,8 @@ def main():
             base = dev_buf.data_ptr()
             plan.seqinfo, plan.items = base, base + B * 16
             placement[0] = "device"
+        if queue is not None:
+            plan.queue = queue.data_ptr()
         if fused:
             nonlocal counters
             if counters is None:
@@ -427,7 +432,7 @@ def main():
                        "mean_seqlen": float(seqlens_host.mean()), "page_size": w.page_size,
                        "kv_bytes_per_step": int(kvb), "gpus": 1, "layout": args.layout,
                        "cache_flush": args.flush, "plan_mem": placement[0],
-                       "with_append": bool(args.with_append),
+                       "with_append": bool(args.with_append), "queue": args.queue,
                        "merge": args.merge},
             "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
             "tokens_per_s": round(tokens / (ms * 1e-3), 1),

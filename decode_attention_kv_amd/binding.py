@@ -56,7 +56,8 @@ class Plan(Structure):
     _fields_ = [("n_items", c_int32), ("batch", c_int32), ("n_groups", c_int32),
                 ("q_len", c_int32), ("max_splits", c_int32), ("n_partial_slots", c_int32),
                 ("items", c_void_p), ("seqinfo", c_void_p), ("counters", c_void_p),
-                ("items_host", c_void_p), ("seqinfo_host", c_void_p), ("inline_ok", c_int32)]
+                ("items_host", c_void_p), ("seqinfo_host", c_void_p), ("inline_ok", c_int32),
+                ("queue", c_void_p)]
 
 
 ATTN_PLAN_INLINE_MAX = 800
@@ -212,7 +213,7 @@ class DevicePlan:
     """A host plan plus its device copy (keeps the device arrays alive)."""
 
     def __init__(self, shape_: Shape, seqlens_host, device, cu_count=256, chunk_tokens=0,
-                 fused_merge=False, inline=False):
+                 fused_merge=False, inline=False, queue=None):
         import torch
 
         seqlens_host = np.ascontiguousarray(seqlens_host, dtype=np.int32)
@@ -246,6 +247,10 @@ class DevicePlan:
             n = attn_decode_counter_count(plan, shape_.h_q)
             self.counters = torch.zeros(max(n, 1), dtype=torch.int32, device=device)
             plan.counters = self.counters.data_ptr()
+        # optional work-queue counter (zero before first use; calls leave it zero)
+        self.queue = queue
+        if queue is not None:
+            plan.queue = queue.data_ptr()
         self.plan = plan
 
 
@@ -253,7 +258,7 @@ def decode(kind: str, q, pool0, pool1, rope, page_table, seqlens, seqlens_host, 
            scale: float, causal: bool = False, rope_theta: float = 0.0, d_rope: int = 0,
            out=None, lse=None, chunk_tokens: int = 0, cu_count: int = 256, plan=None,
            workspace=None, stream=None, defer_merge: bool = False, fused_merge: bool = False,
-           inline_plan: bool = False):
+           inline_plan: bool = False, queue=None):
     """Run one decode through the native library on torch tensors.
 
     kind: "gqa" | "gta" | "latent".  q [B, T, H, Dq]; pools as in the header.
@@ -263,6 +268,8 @@ def decode(kind: str, q, pool0, pool1, rope, page_table, seqlens, seqlens_host, 
     merge counters and the decode kernel merges split rows itself; otherwise
     the merge is a second launch on the stream.  With ``inline_plan`` a new
     plan is passed in the kernels' launch arguments instead of device arrays.
+    ``queue`` (a zeroed int32 device tensor of one element) lets the GQA
+    streaming kernel hand items out dynamically.
     """
     import torch
 
@@ -273,7 +280,7 @@ def decode(kind: str, q, pool0, pool1, rope, page_table, seqlens, seqlens_host, 
         dtype = ATTN_BF16 if pool0.dtype == torch.bfloat16 else ATTN_FP32
         sh = shape(kind, dtype, B, T, H, groups, width, d_rope, pool0.shape[1], causal)
         plan = DevicePlan(sh, seqlens_host, q.device, cu_count=cu_count, chunk_tokens=chunk_tokens,
-                          fused_merge=fused_merge, inline=inline_plan)
+                          fused_merge=fused_merge, inline=inline_plan, queue=queue)
     need = attn_decode_workspace_size(plan.plan, H, d_v)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)

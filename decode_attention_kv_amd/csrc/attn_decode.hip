@@ -59,6 +59,20 @@ __global__ __launch_bounds__(256) void combine_kernel(Params p) {
 // host side
 bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
+// workgroups of `per_cu` per CU the current device keeps resident
+int resident_slots(int per_cu) {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    cus[dev] = n;
+  }
+  return cus[dev] * per_cu;
+}
+
 // the plan's device arrays, or a plan to pass in the launch arguments
 bool plan_on_device(const attn_plan_t* plan) { return plan->items && plan->seqinfo; }
 bool plan_inline(const attn_plan_t* plan) {
@@ -239,6 +253,10 @@ int attn_decode_gqa(const attn_paged_kv_t* kv, const void* q, void* out, float* 
     // the streaming kernel merges split rows itself when the plan carries
     // counters (and the merge is not deferred); otherwise a merge launch
     p.fuse_merge = (!(flags & ATTN_DEFER_MERGE) && plan->counters) ? 1 : 0;
+    if (plan->queue) {
+      p.queue = plan->queue;
+      p.queue_base = resident_slots(kc.wgs_per_cu);
+    }
     st = run_narrow(GQA, d, p, plan->n_items, h_kv, kc.stages, stream);
     if (st != ATTN_OK || (flags & ATTN_DEFER_MERGE) || p.fuse_merge) return st;
     return d == 128 ? launch_combine<__bf16, 128>(p, plan, stream)

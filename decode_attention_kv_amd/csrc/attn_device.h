@@ -42,6 +42,8 @@ struct Params {
   float* lse_part;
   int32_t* flags;     // latent streaming kernel: per-workgroup fix-up flags
   uint32_t* counters; // merge arrival counters (streaming kernels)
+  uint32_t* queue;    // work-queue counter (GQA streaming kernel) or null
+  int32_t queue_base; // items handed out statically (= resident workgroups)
   int32_t fuse_merge; // streaming kernels: the last split workgroup merges
   const int32_t* items;
   const int32_t* seqinfo;

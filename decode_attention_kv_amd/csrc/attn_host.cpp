@@ -248,6 +248,7 @@ int attn_decode_plan(const attn_shape_t* shape, const int32_t* seqlens_host, int
   plan->items = nullptr;
   plan->seqinfo = nullptr;
   plan->counters = nullptr;
+  plan->queue = nullptr;
   plan->items_host = items_host;
   plan->seqinfo_host = seqinfo_host;
   plan->inline_ok = (4 * (int64_t)batch + (int64_t)chunks.size() <= ATTN_PLAN_INLINE_MAX &&

@@ -248,12 +248,16 @@ void decode_narrow(Params p) {
   // The plan lists the groups of one (sequence, chunk) consecutively; with
   // gsz > 1 they are mapped to blocks 8 apart so they share one XCD's L2
   // (GTA's RoPE key rows are read by every group); gsz = 1 keeps plan order.
+  // With a work queue (GQA) the grid holds as many workgroups as the GPU
+  // keeps resident: block i takes item i first, and later items go to the
+  // workgroups that finish first, whatever their XCD.
   const int gsz = p.row_blocks;  // items per unit kept on one XCD
   const int bid = blockIdx.x;
   const int blk = bid / (8 * gsz);
   const int rem = bid - blk * 8 * gsz;
-  const int item = (blk * 8 + (rem & 7)) * gsz + (rem >> 3);
-  if (item >= p.n_items) return;
+  __shared__ int next_item;
+  uint32_t ticket = 0;
+  for (int item = (blk * 8 + (rem & 7)) * gsz + (rem >> 3); item < p.n_items;) {
   const PlanItem pi = load_item(p, item);
   const int b = pi.b, j = pi.j, split = pi.split, t0 = pi.t0;
   const int n_splits = pi.n_splits, slot_base = pi.slot_base, L = pi.L, chunk = pi.chunk;
@@ -565,6 +569,10 @@ void decode_narrow(Params p) {
         // wait until this tile's loads (issued STAGES-1 tiles ago) landed
         constexpr int ahead = (STAGES - 1) * (G::LOADS + (SP ? 1 : 0));
         __builtin_amdgcn_s_waitcnt((ahead & 15) | ((ahead >> 4) << 14) | (0x7 << 4) | (0xf << 8));
+        // the next item's ticket, drawn as the last tile starts so that the
+        // atomic's round trip overlaps this tile's arithmetic
+        if (p.queue && t + u == n_tiles - 1 && tid == 0)
+          ticket = __hip_atomic_fetch_add(p.queue, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         compute(t + u, u);
       }
     }
@@ -648,6 +656,22 @@ void decode_narrow(Params p) {
   if (n_splits > 1 && p.fuse_merge)
     arrive_and_merge<D>(p, p.counters + (int64_t)b * (p.h_q / p.g) + j, &merge_last, b, j, 0,
                         p.rows, n_splits, slot_base);
+
+  // next item from the queue.  Every processed item draws one ticket, so
+  // tickets 0 .. n_items - 1 are drawn in all; the draw of the last one
+  // returns the counter to zero for the next call.
+  if (!p.queue) break;
+  if (tid == 0) {
+    if (n_tiles == 0)
+      ticket = __hip_atomic_fetch_add(p.queue, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (ticket == (uint32_t)(p.n_items - 1))
+      __hip_atomic_store(p.queue, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    next_item = p.queue_base + (int)ticket;
+  }
+  __syncthreads();  // the ring and merge buffers are free, next_item is visible
+  item = next_item;
+  __syncthreads();  // every thread has read next_item before it changes
+  }
 }
 
 }  // namespace narrow
@@ -664,7 +688,12 @@ int launch_narrow_s(Params p, int n_items, int groups, hipStream_t stream) {
     // round-robin like any item, which balances the XCDs
     const int gsz = KIND == GTA ? groups : 1;
     p.row_blocks = gsz;
-    const int blocks = (n_items + 8 * gsz - 1) / (8 * gsz) * 8 * gsz;
+    int blocks = (n_items + 8 * gsz - 1) / (8 * gsz) * 8 * gsz;
+    if (p.queue && KIND == GQA && p.queue_base > 0 && p.queue_base < n_items) {
+      blocks = p.queue_base;  // resident workgroups; the rest come from the queue
+    } else {
+      p.queue = nullptr;
+    }
     hipLaunchKernelGGL((narrow::decode_narrow<KIND, D, DR, RT, S, SP>), dim3(blocks),
                        dim3(narrow::NW * 64), 0, stream, p);
     return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;

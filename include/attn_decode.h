@@ -147,7 +147,19 @@ typedef struct {
   const int32_t* items_host;   /* the host arrays attn_decode_plan filled        */
   const int32_t* seqinfo_host;
   int32_t inline_ok;       /* 1: the plan fits the kernels' launch arguments     */
+  uint32_t* queue;         /* DEVICE work-queue counter or NULL (see below)      */
 } attn_plan_t;
+
+/*
+ * queue: with a non-NULL device uint32 (zero before its first use) the GQA
+ * streaming kernel launches only as many workgroups as the GPU keeps
+ * resident; each takes one item of the plan's order first and then draws
+ * the next unstarted item from this counter as it finishes, so work moves
+ * to whichever XCD frees up first.  Every complete call leaves the counter
+ * zero, so one counter serves every later call; calls sharing it must not
+ * overlap.  NULL (what attn_decode_plan stores): a fixed item per workgroup.
+ * Other kernels ignore it.
+ */
 
 /*
  * Launch-argument plans.  A plan needs 4 * batch + n_items / n_groups int32

@@ -370,3 +370,39 @@ def test_launch_argument_plan_matches_device_plan(name, page_size):
 def w_pages_ok(name):
     # fp32 shapes run on the general kernel at their own page size
     return SMALL[name].dtype == "bf16"
+
+
+@pytest.mark.parametrize("page_size,chunk", [(64, 64), (1, 128), (16, 128)])
+def test_work_queue_matches_fixed_assignment(page_size, chunk):
+    """More items than resident workgroups: with a work-queue counter the GQA
+    kernel hands out items dynamically; the result is bit-identical to the
+    fixed assignment, matches the oracle, and the counter returns to zero
+    after each call (two calls in a row share it)."""
+    w = SMALL["gqa_llama8b"].with_(batch=9, seqlen_lo=500, seqlen_hi=2000, max_seqlen=2048,
+                                   page_size=page_size)
+    print(f"[queue] P={page_size} chunk={chunk}", flush=True)
+    inp = synth.make_inputs(w)
+    d = H.to_device(w, inp)
+    o1, l1, plan1 = H.run(w, d, chunk_tokens=chunk)
+    assert plan1.plan.n_items > 512
+    queue = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for rep in range(2):
+        o2, l2, _ = H.run(w, d, chunk_tokens=chunk, queue=queue)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), rep
+        assert int(queue.item()) == 0, rep
+    ref, ref_lse = oracle.decode(w, inp)
+    H.compare(H.to_np(o2), H.to_np(l2), ref, ref_lse, H.value_max(w, inp), "queue")
+
+
+def test_work_queue_full_size():
+    w = W["gqa_llama8b"]
+    inp = synth.make_inputs(w)
+    d = H.to_device(w, inp)
+    queue = torch.zeros(1, dtype=torch.int32, device="cuda")
+    o1, l1, _ = H.run(w, d)
+    o2, l2, plan = H.run(w, d, queue=queue)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2) and int(queue.item()) == 0
+    del d
+    torch.cuda.empty_cache()
