@@ -32,12 +32,36 @@ __global__ __launch_bounds__(256) void combine_kernel(Params p) {
   const int row = blockIdx.x * RPB + threadIdx.x / TPR;
   if (row >= rows_total) return;
   const int c4 = (threadIdx.x % TPR) * 4;
+  // the first NB splits' partials are loaded at once (one memory round
+  // trip); the arithmetic runs in split order as below
+  constexpr int NB = 4;
+  float ls[NB];
+  f32x4 os[NB];
+#pragma unroll
+  for (int s = 0; s < NB; ++s) {
+    if (s < n) {
+      const int64_t pr = (int64_t)(base + s) * rows_total + row;
+      ls[s] = lse_part[pr];
+      os[s] = *reinterpret_cast<const f32x4*>(o_part + pr * DV + c4);
+    }
+  }
   float M = -INFINITY;
-  for (int s = 0; s < n; ++s) M = fmaxf(M, lse_part[(int64_t)(base + s) * rows_total + row]);
+#pragma unroll
+  for (int s = 0; s < NB; ++s)
+    if (s < n) M = fmaxf(M, ls[s]);
+  for (int s = NB; s < n; ++s) M = fmaxf(M, lse_part[(int64_t)(base + s) * rows_total + row]);
   const float Ms = (M == -INFINITY) ? 0.f : M;
   f32x4 a = {0.f, 0.f, 0.f, 0.f};
   float W = 0.f;
-  for (int s = 0; s < n; ++s) {
+#pragma unroll
+  for (int s = 0; s < NB; ++s) {
+    if (s < n) {
+      const float w = __expf(ls[s] - Ms);
+      W += w;
+      a += w * os[s];
+    }
+  }
+  for (int s = NB; s < n; ++s) {
     const int64_t pr = (int64_t)(base + s) * rows_total + row;
     const float w = __expf(lse_part[pr] - Ms);
     W += w;
