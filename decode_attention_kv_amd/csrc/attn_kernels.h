@@ -101,7 +101,9 @@ inline KernelChoice choose_kernel(const attn_shape_t& sh) {
     const int wg_rows = 32 * wide_rt(sh.head_dim, k.rows);
     k.row_blocks = (k.rows + wg_rows - 1) / wg_rows;
     k.same_xcd_groups = true;  // groups share RoPE rows, row blocks latent rows
-    k.rmax = 1.25;
+    // a latent workgroup streams at its own pace: timelines show the same
+    // per-workgroup rate with 182 or 256 of them active
+    k.rmax = 1.0;
     k.fixed_tiles = 8.0;
     return k;
   }
