@@ -123,14 +123,9 @@ int ilog2_pow2(int v) {
   return s;
 }
 
-struct Common {
-  int elem;
-  int d_v;
-};
-
 int validate(const attn_paged_kv_t* kv, const void* q, const void* out, int q_len, int h_q,
              int groups, int flags, const attn_plan_t* plan, const void* ws, size_t ws_bytes, int d_v,
-             int pool_width, bool need_pool1, bool need_rope, int rope_width) {
+             bool need_pool1, bool need_rope) {
   if (!kv || !q || !out || !plan) return ATTN_ERR_INVALID_ARG;
   if (!kv->pool0 || !kv->page_table || !kv->seqlens) return ATTN_ERR_INVALID_ARG;
   if (need_pool1 && !kv->pool1) return ATTN_ERR_INVALID_ARG;
@@ -158,8 +153,6 @@ int validate(const attn_paged_kv_t* kv, const void* q, const void* out, int q_le
       return ATTN_ERR_INVALID_ARG;
     if (kv->rope_token_stride < 0 || kv->rope_page_stride < 0) return ATTN_ERR_INVALID_ARG;
   }
-  (void)pool_width;
-  (void)rope_width;
   const size_t need = attn_decode_workspace_size(plan, h_q, d_v);
   if (need > 0 && (!ws || ws_bytes < need || ((uintptr_t)ws & 255u)))
     return ATTN_ERR_WORKSPACE;
@@ -266,7 +259,7 @@ extern "C" {
 int attn_decode_gqa(const attn_paged_kv_t* kv, const void* q, void* out, float* lse, int q_len,
                     int h_q, int h_kv, int d, float softmax_scale, int flags,
                     const attn_plan_t* plan, void* ws, size_t ws_bytes, hipStream_t stream) {
-  int st = validate(kv, q, out, q_len, h_q, h_kv, flags, plan, ws, ws_bytes, d, d, true, false, 0);
+  int st = validate(kv, q, out, q_len, h_q, h_kv, flags, plan, ws, ws_bytes, d, true, false);
   if (st != ATTN_OK) return st;
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
   Params p;
@@ -295,7 +288,7 @@ int attn_decode_gta(const attn_paged_kv_t* kv, const void* q, void* out, float* 
                     int h_q, int h_kv, int d, int d_rope, int n_rope_heads, float rope_theta,
                     float softmax_scale, int flags, const attn_plan_t* plan, void* ws,
                     size_t ws_bytes, hipStream_t stream) {
-  int st = validate(kv, q, out, q_len, h_q, h_kv, flags, plan, ws, ws_bytes, d, d, false, true, d_rope);
+  int st = validate(kv, q, out, q_len, h_q, h_kv, flags, plan, ws, ws_bytes, d, false, true);
   if (st != ATTN_OK) return st;
   if (n_rope_heads != 1 || d_rope <= 0 || d_rope >= d) return ATTN_ERR_INVALID_ARG;
   if (kv->dtype != ATTN_BF16 || d != 128 || d_rope != 64) return ATTN_ERR_UNSUPPORTED;
@@ -317,7 +310,7 @@ int attn_decode_latent(const attn_paged_kv_t* kv, const void* q, void* out, floa
                        int q_len, int h_q, int h_c, int d_c, int d_rope, float softmax_scale,
                        int flags, const attn_plan_t* plan, void* ws, size_t ws_bytes,
                        hipStream_t stream) {
-  int st = validate(kv, q, out, q_len, h_q, h_c, flags, plan, ws, ws_bytes, d_c, d_c, false, true, d_rope);
+  int st = validate(kv, q, out, q_len, h_q, h_c, flags, plan, ws, ws_bytes, d_c, false, true);
   if (st != ATTN_OK) return st;
   if (kv->dtype != ATTN_BF16 || d_rope != 64 || (d_c != 512 && d_c != 256))
     return ATTN_ERR_UNSUPPORTED;
