@@ -257,6 +257,24 @@ void decode_narrow(Params p) {
   const int rem = bid - blk * 8 * gsz;
   __shared__ int next_item;
   uint32_t ticket = 0;
+
+  // GTA RoPE table per frequency k = 8 grp + u: revolutions per position as
+  // hi + lo floats, and cos / sin of one tile (64 positions) of it
+  __shared__ float rope_tab[KIND == GTA ? 32 * 4 : 1];
+  if constexpr (KIND == GTA) {
+    if (tid < 32) {
+      const float hi = p.rope_hi[tid], lo = p.rope_lo[tid];
+      float r = hi * (float)KTILE;  // exact (a power of two)
+      r -= floorf(r);
+      r += lo * (float)KTILE;
+      r -= floorf(r);
+      rope_tab[4 * tid + 0] = hi;
+      rope_tab[4 * tid + 1] = lo;
+      rope_tab[4 * tid + 2] = __builtin_amdgcn_cosf(r);
+      rope_tab[4 * tid + 3] = __builtin_amdgcn_sinf(r);
+    }
+    __syncthreads();
+  }
   for (int item = (blk * 8 + (rem & 7)) * gsz + (rem >> 3); item < p.n_items;) {
   const PlanItem pi = load_item(p, item);
   const int b = pi.b, j = pi.j, split = pi.split, t0 = pi.t0;
@@ -350,14 +368,11 @@ void decode_narrow(Params p) {
     }
   };
 
-  // RoPE frequencies of this lane's 8 pairs (entries 8 grp + u), hoisted so
-  // no per-lane kernel-argument loads sit inside the streaming loop
-  float rh[8], rl[8];
-#pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    rh[u] = (KIND == GTA) ? p.rope_hi[grp * 8 + u] : 0.f;
-    rl[u] = (KIND == GTA) ? p.rope_lo[grp * 8 + u] : 0.f;
-  }
+  // this lane's RoPE frequencies are entries 8 grp + u of rope_tab; the
+  // rotation of its key (key0 + col) is kept as sin / cos per frequency,
+  // advanced by one tile per slice and recomputed exactly every 16 tiles
+  const float* rtab = rope_tab + (KIND == GTA ? 32 * grp : 0);
+  float rsn[8], rcs[8];
 
   // ---- query B operands in registers (rotated for GTA)
   bf16x8 qreg[RT][NKC];
@@ -378,7 +393,7 @@ void decode_narrow(Params p) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           float sn, cs;
-          rope_sincos(qpos, rh[u], rl[u], sn, cs);
+          rope_sincos(qpos, rtab[4 * u], rtab[4 * u + 1], sn, cs);
           const float x = (float)qreg[rt][c0][u], y = (float)qreg[rt][c0 + 1][u];
           qreg[rt][c0][u] = (__bf16)(x * cs - y * sn);
           qreg[rt][c0 + 1][u] = (__bf16)(x * sn + y * cs);
@@ -475,14 +490,27 @@ void decode_narrow(Params p) {
       for (int c = 0; c < c0; ++c) mma(kread(c), c);
       bf16x8 ka = kread(c0), kb = kread(c0 + 1);
       if (p.rope_on) {
-        const float kpos = (float)(key0 + col);
+        if ((t & 15) == 0) {
+          // exact angle of this lane's key (first tile of 16)
+          const float kpos = (float)(key0 + col);
+#pragma unroll
+          for (int u2 = 0; u2 < 8; ++u2)
+            rope_sincos(kpos, rtab[4 * u2], rtab[4 * u2 + 1], rsn[u2], rcs[u2]);
+        } else {
+          // one tile further: angle addition with the tile's cos / sin
+#pragma unroll
+          for (int u2 = 0; u2 < 8; ++u2) {
+            const float c1 = rtab[4 * u2 + 2], s1 = rtab[4 * u2 + 3];
+            const float sn = rsn[u2], cs = rcs[u2];
+            rsn[u2] = fmaf(sn, c1, cs * s1);
+            rcs[u2] = fmaf(cs, c1, -(sn * s1));
+          }
+        }
 #pragma unroll
         for (int u2 = 0; u2 < 8; ++u2) {
-          float sn, cs;
-          rope_sincos(kpos, rh[u2], rl[u2], sn, cs);
           const float x = (float)ka[u2], y = (float)kb[u2];
-          ka[u2] = (__bf16)(x * cs - y * sn);
-          kb[u2] = (__bf16)(x * sn + y * cs);
+          ka[u2] = (__bf16)(x * rcs[u2] - y * rsn[u2]);
+          kb[u2] = (__bf16)(x * rsn[u2] + y * rcs[u2]);
         }
       }
       mma(ka, c0);
