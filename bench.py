@@ -194,6 +194,12 @@ def main():
     ap.add_argument("--with-append", action="store_true",
                     help="each step first writes the q_len newest cache rows of every sequence "
                          "(attn_kv_append, the same rows again) before planning and decoding")
+    ap.add_argument("--with-absorb", action="store_true",
+                    help="latent workloads: each step also forms the decode's query from "
+                         "q_nope / q_rope with per-head key up-projections (128 -> d_c) before "
+                         "the decode and projects the latent output to 128 per head after it "
+                         "(attn_latent_absorb_query / attn_latent_project_output, random "
+                         "weights)")
     ap.add_argument("--queue", choices=["on", "off"], default="off",
                     help="on: the GQA kernel hands items out through a work-queue counter")
     ap.add_argument("--set", action="append", default=[], metavar="FIELD=VALUE",
@@ -332,6 +338,20 @@ def main():
                     0 if rows["rope"] is None else w.d_rope,
                     None if rows["rope"] is None else rows["rope"].data_ptr(), 0.0)
 
+    if args.with_absorb:
+        if w.kind != "latent":
+            print("--with-absorb applies to latent workloads", file=sys.stderr)
+            sys.exit(2)
+        D_NOPE = D_V = 128
+        pin = synth.make_projection_inputs(B * T, H, D_NOPE, d_v, w.d_rope, D_V, seed=w.seed + 1)
+
+        def _bf(a):
+            return torch.from_numpy(np.ascontiguousarray(a)).to(torch.bfloat16).to(dev)
+
+        q_nope, q_rope, w_uk, w_uv = (_bf(pin["q_nope"]), _bf(pin["q_rope"]), _bf(pin["w_uk"]),
+                                      _bf(pin["w_uv"]))
+        out_v = torch.empty((B * T, H, D_V), dtype=torch.bfloat16, device=dev)
+
     def step(k, evs, inner):
         """One step: plan (host) + upload, decode (which merges split rows
         itself, or a merge launch after it).  evs = [start, before decode,
@@ -344,6 +364,12 @@ def main():
             if st != binding.ATTN_OK:
                 raise binding.AttnError(st, "attn_kv_append")
         plan, slot = make_plan(k)
+        if args.with_absorb:  # the decode's query, written in place
+            st = binding.attn_latent_absorb_query(q_nope.data_ptr(), q_rope.data_ptr(),
+                                                  w_uk.data_ptr(), q.data_ptr(), B * T, H,
+                                                  D_NOPE, d_v, w.d_rope, s)
+            if st != binding.ATTN_OK:
+                raise binding.AttnError(st, "attn_latent_absorb_query")
         if inner:
             evs[1].record(stream)
         if w.kind == "gqa":
@@ -367,7 +393,12 @@ def main():
                                            out.data_ptr(), lse.data_ptr(), s)
             if st != binding.ATTN_OK:
                 raise binding.AttnError(st, "merge")
-        if inner and fused:
+        if args.with_absorb:
+            st = binding.attn_latent_project_output(out.data_ptr(), w_uv.data_ptr(),
+                                                    out_v.data_ptr(), B * T, H, d_v, D_V, s)
+            if st != binding.ATTN_OK:
+                raise binding.AttnError(st, "attn_latent_project_output")
+        if inner and fused and not args.with_absorb:
             evs[3] = evs[2]  # the step ends with the decode kernel
         else:
             evs[3].record(stream)
@@ -434,7 +465,8 @@ def main():
                        "mean_seqlen": float(seqlens_host.mean()), "page_size": w.page_size,
                        "kv_bytes_per_step": int(kvb), "gpus": 1, "layout": args.layout,
                        "cache_flush": args.flush, "plan_mem": placement[0],
-                       "with_append": bool(args.with_append), "queue": args.queue,
+                       "with_append": bool(args.with_append),
+                       "with_absorb": bool(args.with_absorb), "queue": args.queue,
                        "merge": args.merge},
             "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
             "tokens_per_s": round(tokens / (ms * 1e-3), 1),

@@ -18,7 +18,7 @@ LIB = os.path.join(PKG, "libattn_decode.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 SOURCES = ("attn_host.cpp", "attn_decode.hip", "attn_general.hip", "attn_narrow.hip",
-           "attn_wide.hip", "attn_append.hip")
+           "attn_wide.hip", "attn_append.hip", "attn_absorb.hip")
 
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-I" + os.path.join(ROOT, "include"),

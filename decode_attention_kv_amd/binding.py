@@ -109,6 +109,12 @@ def lib():
     L.attn_kv_append.restype = c_int
     L.attn_paged_kv_check.argtypes = [POINTER(PagedKV)]
     L.attn_paged_kv_check.restype = c_int
+    L.attn_latent_absorb_query.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int,
+                                           c_int, c_int, c_int, c_void_p]
+    L.attn_latent_absorb_query.restype = c_int
+    L.attn_latent_project_output.argtypes = [c_void_p, c_void_p, c_void_p, c_int, c_int, c_int,
+                                             c_int, c_void_p]
+    L.attn_latent_project_output.restype = c_int
     _lib = L
     return L
 
@@ -174,6 +180,16 @@ def attn_kv_append(kv, q_len, heads, width, new0, new1, d_rope, new_rope, rope_t
 
 def attn_paged_kv_check(kv: PagedKV) -> int:
     return lib().attn_paged_kv_check(ctypes.byref(kv))
+
+
+def attn_latent_absorb_query(q_nope, q_rope, w_uk, q_out, n_tok, h_q, d_nope, d_c, d_rope,
+                             stream) -> int:
+    return lib().attn_latent_absorb_query(q_nope, q_rope, w_uk, q_out, n_tok, h_q, d_nope, d_c,
+                                          d_rope, stream)
+
+
+def attn_latent_project_output(o_lat, w_uv, out, n_tok, h_q, d_c, d_v, stream) -> int:
+    return lib().attn_latent_project_output(o_lat, w_uv, out, n_tok, h_q, d_c, d_v, stream)
 
 
 # ------------------------------------------------------------ torch plumbing
@@ -326,6 +342,56 @@ def kv_append(pool0, pool1, rope, page_table, seqlens, new0, new1=None, new_rope
                         float(rope_theta), s)
     if st != ATTN_OK:
         raise AttnError(st, "attn_kv_append")
+
+
+def absorb_query(q_nope, q_rope, w_uk, out=None, stream=None):
+    """Latent decode query [.., h_q, d_c + d_r] from q_nope [.., h_q, d_nope],
+    q_rope [.., h_q, d_r] (or None) and w_uk [h_q, d_c, d_nope], all bf16
+    (attn_latent_absorb_query); leading dims are the step's tokens."""
+    import torch
+
+    h_q, d_nope = q_nope.shape[-2], q_nope.shape[-1]
+    d_c = w_uk.shape[1]
+    d_rope = 0 if q_rope is None else q_rope.shape[-1]
+    lead = q_nope.shape[:-2]
+    n_tok = int(np.prod(lead)) if len(lead) else 1
+    for t in (q_nope, q_rope, w_uk):
+        if t is not None and (not t.is_contiguous() or t.dtype != torch.bfloat16):
+            raise ValueError("inputs must be contiguous bfloat16")
+    if tuple(w_uk.shape) != (h_q, d_c, d_nope):
+        raise ValueError("w_uk must be [h_q, d_c, d_nope]")
+    if out is None:
+        out = torch.empty(*lead, h_q, d_c + d_rope, dtype=torch.bfloat16, device=q_nope.device)
+    s = (stream if stream is not None else torch.cuda.current_stream(q_nope.device)).cuda_stream
+    st = attn_latent_absorb_query(q_nope.data_ptr(), _ptr(q_rope), w_uk.data_ptr(),
+                                  out.data_ptr(), n_tok, h_q, d_nope, d_c, d_rope, s)
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_latent_absorb_query")
+    return out
+
+
+def project_output(o_lat, w_uv, out=None, stream=None):
+    """Per-head output [.., h_q, d_v] from the latent output o_lat
+    [.., h_q, d_c] and w_uv [h_q, d_v, d_c], bf16 (attn_latent_project_output)."""
+    import torch
+
+    h_q, d_c = o_lat.shape[-2], o_lat.shape[-1]
+    d_v = w_uv.shape[1]
+    lead = o_lat.shape[:-2]
+    n_tok = int(np.prod(lead)) if len(lead) else 1
+    for t in (o_lat, w_uv):
+        if not t.is_contiguous() or t.dtype != torch.bfloat16:
+            raise ValueError("inputs must be contiguous bfloat16")
+    if tuple(w_uv.shape) != (h_q, d_v, d_c):
+        raise ValueError("w_uv must be [h_q, d_v, d_c]")
+    if out is None:
+        out = torch.empty(*lead, h_q, d_v, dtype=torch.bfloat16, device=o_lat.device)
+    s = (stream if stream is not None else torch.cuda.current_stream(o_lat.device)).cuda_stream
+    st = attn_latent_project_output(o_lat.data_ptr(), w_uv.data_ptr(), out.data_ptr(), n_tok, h_q,
+                                    d_c, d_v, s)
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_latent_project_output")
+    return out
 
 
 def merge(plan: DevicePlan, out, lse, workspace, stream=None):

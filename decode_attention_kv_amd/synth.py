@@ -152,6 +152,26 @@ def _normal(rng: np.random.Generator, shape, std: float, dtype: str) -> np.ndarr
     return x
 
 
+def make_projection_inputs(n_tok: int, h_q: int, d_nope: int, d_c: int, d_rope: int, d_v: int,
+                           seed: int, q_std: float = 0.5) -> Dict[str, np.ndarray]:
+    """Seeded inputs of the projections around the latent decode.
+
+    Draw order from ``PCG64(seed)``: q_nope [n_tok, h_q, d_nope], q_rope
+    [n_tok, h_q, d_rope] (None when d_rope is 0), w_uk [h_q, d_c, d_nope],
+    w_uv [h_q, d_v, d_c], o_lat [n_tok, h_q, d_c].  Queries and o_lat are
+    N(0,1)*q_std; weights are random-init N(0, 1/fan_in) (fan_in d_nope for
+    w_uk, d_c for w_uv).  All bfloat16-exact float32.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out: Dict[str, np.ndarray] = {}
+    out["q_nope"] = _normal(rng, (n_tok, h_q, d_nope), q_std, "bf16")
+    out["q_rope"] = _normal(rng, (n_tok, h_q, d_rope), q_std, "bf16") if d_rope else None
+    out["w_uk"] = _normal(rng, (h_q, d_c, d_nope), 1.0 / math.sqrt(d_nope), "bf16")
+    out["w_uv"] = _normal(rng, (h_q, d_v, d_c), 1.0 / math.sqrt(d_c), "bf16")
+    out["o_lat"] = _normal(rng, (n_tok, h_q, d_c), q_std, "bf16")
+    return out
+
+
 def draw_seqlens(w: Workload, rng: np.random.Generator) -> np.ndarray:
     if w.seqlen_lo == w.seqlen_hi:
         return np.full(w.batch, w.seqlen_lo, dtype=np.int32)

@@ -307,6 +307,45 @@ int attn_kv_append(const attn_paged_kv_t* kv, int q_len, int heads, int width, c
                    hipStream_t stream);
 
 /*
+ * Projections around attn_decode_latent (MLA / GLA weight absorption).  The
+ * latent kernel attends in the latent space ("Hardware-Efficient Attention
+ * for Fast Decoding", review page: Core claim, What carries the argument);
+ * the per-head key and value up-projections act on the query and on the
+ * latent output instead of on the cache.  For every token m (the step's
+ * batch * q_len query rows) and query head h, in fp32 from bf16 inputs:
+ *
+ * attn_latent_absorb_query:
+ *   q_out[m][h][n]       = sum_k q_nope[m][h][k] * w_uk[h][n][k],  n < d_c
+ *   q_out[m][h][d_c + j] = q_rope[m][h][j]  (copied),              j < d_rope
+ *   q_nope  [n_tok][h_q][d_nope] bf16, device
+ *   q_rope  [n_tok][h_q][d_rope] bf16, device, already rotated; NULL iff
+ *           d_rope == 0
+ *   w_uk    [h_q][d_c][d_nope] bf16, device: head h's key up-projection
+ *           stored transposed (row n holds the weights of latent dim n)
+ *   q_out   [n_tok][h_q][d_c + d_rope] bf16, device: the latent kernel's q
+ * so that q_out[m][h][0:d_c] . c = q_nope[m][h] . (w_uk[h]^T c) for a latent
+ * row c.
+ *
+ * attn_latent_project_output:
+ *   out[m][h][n] = sum_c o_lat[m][h][c] * w_uv[h][n][c],  n < d_v
+ *   o_lat  [n_tok][h_q][d_c] bf16, device: the latent kernel's output
+ *   w_uv   [h_q][d_v][d_c] bf16, device: head h's value up-projection
+ *   out    [n_tok][h_q][d_v] bf16, device
+ *
+ * Results are rounded to bf16 once.  Requirements: d_nope and (for the
+ * output projection) d_c multiples of 32; d_c (absorb) and d_v multiples
+ * of 64; d_rope a multiple of 8; every pointer 16-byte aligned; n_tok = 0
+ * enqueues nothing and accepts NULL buffers.  The caller owns every buffer; outputs must not alias
+ * inputs.  Returns ATTN_OK once enqueued on `stream`, INVALID_ARG (nothing
+ * enqueued) for inconsistent arguments.
+ */
+int attn_latent_absorb_query(const void* q_nope, const void* q_rope, const void* w_uk,
+                             void* q_out, int n_tok, int h_q, int d_nope, int d_c, int d_rope,
+                             hipStream_t stream);
+int attn_latent_project_output(const void* o_lat, const void* w_uv, void* out, int n_tok,
+                               int h_q, int d_c, int d_v, hipStream_t stream);
+
+/*
  * Host-side consistency check of a descriptor whose page_table and seqlens
  * point to HOST copies: every page a sequence uses is in [0, num_pages) and
  * every length fits the page table.  Returns ATTN_OK or INVALID_ARG.

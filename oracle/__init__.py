@@ -24,6 +24,7 @@ from .attention import (  # noqa: F401
     rope_rotate_half,
 )
 from .append import kv_append, round_bf16  # noqa: F401
+from .absorb import absorb_query, project_output  # noqa: F401
 from .counts import (  # noqa: F401
     kv_bytes,
     kv_bytes_per_token,

@@ -361,3 +361,60 @@ def test_plan_without_device_arrays_needs_inline_ok(kind):
     for fields in (dict(items=None, seqinfo=None, inline_ok=0), dict(seqinfo=None),
                    dict(items=None, seqinfo=None, items_host=None)):
         assert _fake_call(kind, plan_fields=fields, **extra) == binding.ATTN_ERR_INVALID_ARG, fields
+
+
+@pytest.mark.parametrize("case", ["ok_empty", "neg_tok", "no_heads", "nope_not_32", "dc_not_64",
+                                  "rope_not_8", "rope_ptr_without_width", "rope_width_without_ptr",
+                                  "null_w", "unaligned_out"])
+def test_absorb_query_validates_arguments(case):
+    """attn_latent_absorb_query checks its arguments on the host and enqueues
+    nothing on error; an empty step is accepted without a launch (fake,
+    never dereferenced device pointers)."""
+    a = dict(q_nope=0x600000, q_rope=0x610000, w_uk=0x620000, q_out=0x630000, n_tok=1, h_q=16,
+             d_nope=128, d_c=512, d_rope=64)
+    want = binding.ATTN_ERR_INVALID_ARG
+    if case == "ok_empty":
+        a.update(n_tok=0, q_nope=None, q_out=None)
+        want = binding.ATTN_OK
+    elif case == "neg_tok":
+        a["n_tok"] = -1
+    elif case == "no_heads":
+        a["h_q"] = 0
+    elif case == "nope_not_32":
+        a["d_nope"] = 48
+    elif case == "dc_not_64":
+        a["d_c"] = 96
+    elif case == "rope_not_8":
+        a["d_rope"] = 4
+    elif case == "rope_ptr_without_width":
+        a["d_rope"] = 0
+    elif case == "rope_width_without_ptr":
+        a["q_rope"] = None
+    elif case == "null_w":
+        a["w_uk"] = None
+    elif case == "unaligned_out":
+        a["q_out"] = 0x630008
+    st = binding.attn_latent_absorb_query(a["q_nope"], a["q_rope"], a["w_uk"], a["q_out"],
+                                          a["n_tok"], a["h_q"], a["d_nope"], a["d_c"], a["d_rope"],
+                                          None)
+    assert st == want, case
+
+
+@pytest.mark.parametrize("case", ["ok_empty", "dc_not_32", "dv_not_64", "null_out", "unaligned_in"])
+def test_project_output_validates_arguments(case):
+    a = dict(o_lat=0x600000, w_uv=0x620000, out=0x630000, n_tok=1, h_q=16, d_c=512, d_v=128)
+    want = binding.ATTN_ERR_INVALID_ARG
+    if case == "ok_empty":
+        a.update(n_tok=0, out=None)
+        want = binding.ATTN_OK
+    elif case == "dc_not_32":
+        a["d_c"] = 40
+    elif case == "dv_not_64":
+        a["d_v"] = 100
+    elif case == "null_out":
+        a["out"] = None
+    elif case == "unaligned_in":
+        a["o_lat"] = 0x600004
+    st = binding.attn_latent_project_output(a["o_lat"], a["w_uv"], a["out"], a["n_tok"], a["h_q"],
+                                            a["d_c"], a["d_v"], None)
+    assert st == want, case
