@@ -261,7 +261,7 @@ def test_gather_probe_streaming_kernels(kind, page_size):
 
 # ------------------------------------------------------------ full size
 FULL = ["gqa_fp32_tiny", "gqa_llama8b", "gta_8k", "mla", "gla2", "gla2_spec4_128k",
-        "gqa_llama8b@P1", "gla2@P1"]
+        "gqa_llama8b_8k", "gqa4_8k", "mla_spec4_128k", "gqa_llama8b@P1", "gla2@P1"]
 
 
 @pytest.mark.slow
