@@ -299,7 +299,7 @@ int attn_decode_gta(const attn_paged_kv_t* kv, const void* q, void* out, float* 
       choice_for(kv, ATTN_KIND_GTA, q_len, h_q, h_kv, d, d_rope, flags);
   if (kc.narrow) {
     p.fuse_merge = (!(flags & ATTN_DEFER_MERGE) && plan->counters) ? 1 : 0;
-    st = run_narrow(GTA, d, p, plan->n_items, h_kv, kc.stages, stream);
+    st = run_narrow(kc.pair == 2 ? GTA2 : GTA, d, p, plan->n_items, h_kv, kc.stages, stream);
     if (st != ATTN_OK || (flags & ATTN_DEFER_MERGE) || p.fuse_merge) return st;
     return launch_combine<__bf16, 128>(p, plan, stream);
   }

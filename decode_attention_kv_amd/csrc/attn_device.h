@@ -24,7 +24,8 @@ typedef unsigned short u16;
 constexpr int KT = 64;  // keys per tile
 constexpr int kMaxRope = 64;
 
-enum Kind { GQA = 0, GTA = 1, LAT = 2 };
+// GTA2: GTA with two groups per workgroup (their common RoPE rows shared)
+enum Kind { GQA = 0, GTA = 1, LAT = 2, GTA2 = 3 };
 
 struct Params {
   const char* pool0;

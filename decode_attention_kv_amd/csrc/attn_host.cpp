@@ -65,7 +65,7 @@ double simulate(const std::vector<Chunk>& chunks, int groups, const attn_interna
   const int64_t n_items = (int64_t)chunks.size() * groups;
   const bool by_group = kc.same_xcd_groups;
   const int64_t units = by_group ? (int64_t)chunks.size() : n_items;
-  const int per_unit = (by_group ? groups : 1) * std::max(1, kc.row_blocks);
+  const int per_unit = (by_group ? groups / std::max(1, kc.pair) : 1) * std::max(1, kc.row_blocks);
   double makespan = 0.0;
   std::vector<double> heap;
   heap.reserve(slots);

@@ -137,15 +137,18 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 }
 
 template <int KIND, int D, int DR> struct Geo {
-  // per-wave bytes of one stage: K (or tied) rows, V rows (GQA), RoPE rows (GTA)
+  // per-wave bytes of one stage: K (or tied) rows, V rows (GQA), the second
+  // group's tied rows (GTA2), RoPE rows (GTA, GTA2)
+  static constexpr int NT = KIND == GTA2 ? 2 : 1;   // tied groups per stage
   static constexpr int ROW0 = D * 2;                 // K / tied row bytes
   static constexpr int ROWR = DR * 2;                // RoPE row bytes
   static constexpr int K_OFF = 0;
   static constexpr int V_OFF = KW * ROW0;            // GQA only
-  static constexpr int R_OFF = KW * ROW0;            // GTA only
-  static constexpr int WAVE_BYTES = (KIND == GQA) ? 2 * KW * ROW0 : KW * (ROW0 + ROWR);
+  static constexpr int K2_OFF = KW * ROW0;           // GTA2 only
+  static constexpr int R_OFF = NT * KW * ROW0;       // GTA, GTA2
+  static constexpr int WAVE_BYTES = (KIND == GQA) ? 2 * KW * ROW0 : KW * (NT * ROW0 + ROWR);
   static constexpr int STAGE_BYTES = NW * WAVE_BYTES;
-  static constexpr int LOADS = (KIND == GQA) ? 2 * KW * ROW0 / 1024 : KW * (ROW0 + ROWR) / 1024;
+  static constexpr int LOADS = WAVE_BYTES / 1024;
 };
 
 // Per-lane byte offsets of the direct-to-LDS loads of one 16-key slice of
@@ -217,6 +220,9 @@ template <int KIND, int D, int DR, int RT, int STAGES, bool SP>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RT == 2 ? 2 : 1)))
 void decode_narrow(Params p) {
   using G = Geo<KIND, D, DR>;
+  constexpr bool TIED = KIND != GQA;   // tied state + one RoPE key head
+  constexpr bool PAIR = KIND == GTA2;  // two groups per work item
+  static_assert(!(PAIR && SP), "paired groups need pages of at least 16 tokens");
   constexpr int DN = D - DR;          // key entries from the K / tied row
   constexpr int NKC = D / 32;         // 32-dim k-chunks of the score MFMA
   constexpr int NDVT = D / 16;        // 16-wide output tiles
@@ -260,8 +266,8 @@ void decode_narrow(Params p) {
 
   // GTA RoPE table per frequency k = 8 grp + u: revolutions per position as
   // hi + lo floats, and cos / sin of one tile (64 positions) of it
-  __shared__ float rope_tab[KIND == GTA ? 32 * 4 : 1];
-  if constexpr (KIND == GTA) {
+  __shared__ float rope_tab[TIED ? 32 * 4 : 1];
+  if constexpr (TIED) {
     if (tid < 32) {
       const float hi = p.rope_hi[tid], lo = p.rope_lo[tid];
       float r = hi * (float)KTILE;  // exact (a power of two)
@@ -275,8 +281,11 @@ void decode_narrow(Params p) {
     }
     __syncthreads();
   }
-  for (int item = (blk * 8 + (rem & 7)) * gsz + (rem >> 3); item < p.n_items;) {
-  const PlanItem pi = load_item(p, item);
+  // GTA2 works on pairs of plan items: items 2i and 2i + 1 are groups
+  // j, j + 1 (j even) of one (sequence, chunk)
+  const int n_units = PAIR ? p.n_items / 2 : p.n_items;
+  for (int item = (blk * 8 + (rem & 7)) * gsz + (rem >> 3); item < n_units;) {
+  const PlanItem pi = load_item(p, PAIR ? 2 * item : item);
   const int b = pi.b, j = pi.j, split = pi.split, t0 = pi.t0;
   const int n_splits = pi.n_splits, slot_base = pi.slot_base, L = pi.L, chunk = pi.chunk;
   const int t_end = min(t0 + chunk, L);
@@ -285,15 +294,18 @@ void decode_narrow(Params p) {
   const int pmask = (1 << p.page_shift) - 1;
   const int32_t* pt_row = p.page_table + (int64_t)b * p.max_pages;
 
-  // rows of this lane (every wave holds every row)
+  // rows of this lane (every wave holds every row); GTA2: rows
+  // [0, p.rows) belong to group j, rows [p.rows, 2 p.rows) to group j + 1
   int tq[RT], hq[RT], qlimit[RT];
-  bool row_ok[RT];
+  bool row_ok[RT], row_b[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int row = rt * 16 + col;
-    row_ok[rt] = row < p.rows;
-    tq[rt] = row_ok[rt] ? row / p.g : 0;
-    hq[rt] = j * p.g + (row_ok[rt] ? row - tq[rt] * p.g : 0);
+    row_ok[rt] = row < (PAIR ? 2 : 1) * p.rows;
+    row_b[rt] = PAIR && row >= p.rows;
+    const int rr = row_b[rt] ? row - p.rows : row;
+    tq[rt] = row_ok[rt] ? rr / p.g : 0;
+    hq[rt] = (j + (row_b[rt] ? 1 : 0)) * p.g + (row_ok[rt] ? rr - tq[rt] * p.g : 0);
     qlimit[rt] = (p.causal && row_ok[rt]) ? L - p.q_len + tq[rt] : 0x7fffffff;
   }
 
@@ -312,7 +324,7 @@ void decode_narrow(Params p) {
   SliceDMA<G::ROW0> dma0;
   SliceDMA<(DR > 0 ? G::ROWR : 16)> dmar;
   dma0.init(p.token_stride, lane);
-  if constexpr (KIND == GTA) dmar.init(p.rtoken_stride, lane);
+  if constexpr (TIED) dmar.init(p.rtoken_stride, lane);
 
   // small pages: the page ids of this wave's 16 keys of tile x (clamped to
   // the last tile, each key to the last row), one 4-byte load per lane
@@ -359,6 +371,7 @@ void decode_narrow(Params p) {
     // past the end, kc is that row and slot0 its 16-aligned block)
     const int v = min((key0 <= t_last) ? valid : ((kc & pmask) - slot0 + 1), KW);
     dma0.issue_clamped(dst + G::K_OFF, b0, v, p.token_stride);
+    if constexpr (PAIR) dma0.issue_clamped(dst + G::K2_OFF, b0 + p.head_stride * 2, v, p.token_stride);
     if constexpr (KIND == GQA) {
       dma0.issue_clamped(dst + G::V_OFF, p.pool1 + row0 * 2, v, p.token_stride);
     } else {
@@ -371,7 +384,7 @@ void decode_narrow(Params p) {
   // this lane's RoPE frequencies are entries 8 grp + u of rope_tab; the
   // rotation of its key (key0 + col) is kept as sin / cos per frequency,
   // advanced by one tile per slice and recomputed exactly every 16 tiles
-  const float* rtab = rope_tab + (KIND == GTA ? 32 * grp : 0);
+  const float* rtab = rope_tab + (TIED ? 32 * grp : 0);
   float rsn[8], rcs[8];
 
   // ---- query B operands in registers (rotated for GTA)
@@ -386,7 +399,7 @@ void decode_narrow(Params p) {
       if (row_ok[rt]) raw = *reinterpret_cast<const uint4*>(qrow + c * 32 + grp * 8);
       qreg[rt][c] = __builtin_bit_cast(bf16x8, raw);
     }
-    if constexpr (KIND == GTA) {
+    if constexpr (TIED) {
       if (p.rope_on) {
         constexpr int c0 = DN / 32;
         const float qpos = (float)(L - p.q_len + tq[rt]);
@@ -478,17 +491,29 @@ void decode_narrow(Params p) {
       for (int dt = 0; dt < NDVT; ++dt) va_addr[dt] = vbase + v_off[dt];
       slice_reads<NKC, NDVT>(ka_addr, va_addr, kraw, vraw);
     }
+    // GTA2: the second group's non-RoPE K chunks and V^T tiles (the RoPE
+    // chunks read above serve both groups)
+    constexpr int NKB = PAIR ? DN / 32 : 1;
+    u32x4_t kraw2[NKB];
+    u64_t vraw2[PAIR ? NDVT : 1];
+    if constexpr (PAIR) {
+      const uint32_t sbase = lds_addr(sb);
+      uint32_t ka_addr[NKB], va_addr[NDVT];
+#pragma unroll
+      for (int c = 0; c < NKB; ++c) ka_addr[c] = sbase + G::K2_OFF + k_off[c];
+#pragma unroll
+      for (int dt = 0; dt < NDVT; ++dt) va_addr[dt] = sbase + G::K2_OFF + v_off[dt];
+      b128_reads<NKB>(ka_addr, kraw2);
+      tr_reads<NDVT>(va_addr, vraw2);
+    }
     auto kread = [&](int c) { return __builtin_bit_cast(bf16x8, kraw[c]); };
     auto mma = [&](bf16x8 a, int c) {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt)
         sa[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[rt][c], sa[rt], 0, 0, 0);
     };
-    if constexpr (KIND == GTA) {
-      constexpr int c0 = DN / 32;
-#pragma unroll
-      for (int c = 0; c < c0; ++c) mma(kread(c), c);
-      bf16x8 ka = kread(c0), kb = kread(c0 + 1);
+    // the RoPE chunks (c0, c0 + 1) of this lane's key, rotated at its position
+    auto rope_keys = [&](bf16x8& ka, bf16x8& kb) {
       if (p.rope_on) {
         if ((t & 15) == 0) {
           // exact angle of this lane's key (first tile of 16)
@@ -513,10 +538,44 @@ void decode_narrow(Params p) {
           kb[u2] = (__bf16)(x * rsn[u2] + y * rcs[u2]);
         }
       }
+    };
+    if constexpr (KIND == GTA) {
+      constexpr int c0 = DN / 32;
+#pragma unroll
+      for (int c = 0; c < c0; ++c) mma(kread(c), c);
+      bf16x8 ka = kread(c0), kb = kread(c0 + 1);
+      rope_keys(ka, kb);
       mma(ka, c0);
       mma(kb, c0 + 1);
 #pragma unroll
       for (int c = c0 + 2; c < NKC; ++c) mma(kread(c), c);
+    } else if constexpr (PAIR) {
+      // rows of group j score its own non-RoPE chunks, rows of group j + 1
+      // the second group's; both add the shared rotated RoPE chunks
+      static_assert(DN / 32 + 2 == NKC, "tied non-RoPE chunks, then two RoPE chunks");
+      constexpr int c0 = DN / 32;
+      f32x4 sbn[RT], sr[RT];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) sbn[rt] = sr[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < c0; ++c) {
+        mma(kread(c), c);
+        const bf16x8 kbb = __builtin_bit_cast(bf16x8, kraw2[c]);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+          sbn[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kbb, qreg[rt][c], sbn[rt], 0, 0, 0);
+      }
+      bf16x8 ka = kread(c0), kb = kread(c0 + 1);
+      rope_keys(ka, kb);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        sr[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qreg[rt][c0], sr[rt], 0, 0, 0);
+        sr[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qreg[rt][c0 + 1], sr[rt], 0, 0, 0);
+      }
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sa[rt][i] = (row_b[rt] ? sbn[rt][i] : sa[rt][i]) + sr[rt][i];
     } else {
 #pragma unroll
       for (int c = 0; c < NKC; ++c) mma(kread(c), c);
@@ -577,12 +636,33 @@ void decode_narrow(Params p) {
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) pb[rt][i] = (__bf16)s[rt][i];
+    if constexpr (PAIR) {
+      // each row's probabilities meet its own group's values
+      const bf16x4 zero4 = {};
+      bf16x4 pa[RT], pbb[RT];
 #pragma unroll
-    for (int dt = 0; dt < NDVT; ++dt) {
-      const bf16x4 va = __builtin_bit_cast(bf16x4, vraw[dt]);
+      for (int rt = 0; rt < RT; ++rt) {
+        pa[rt] = row_b[rt] ? zero4 : pb[rt];
+        pbb[rt] = row_b[rt] ? pb[rt] : zero4;
+      }
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-        acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb[rt], acc[rt][dt], 0, 0, 0);
+      for (int dt = 0; dt < NDVT; ++dt) {
+        const bf16x4 va = __builtin_bit_cast(bf16x4, vraw[dt]);
+        const bf16x4 vb = __builtin_bit_cast(bf16x4, vraw2[dt]);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pa[rt], acc[rt][dt], 0, 0, 0);
+          acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vb, pbb[rt], acc[rt][dt], 0, 0, 0);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int dt = 0; dt < NDVT; ++dt) {
+        const bf16x4 va = __builtin_bit_cast(bf16x4, vraw[dt]);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+          acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb[rt], acc[rt][dt], 0, 0, 0);
+      }
     }
   };
 
@@ -681,9 +761,12 @@ void decode_narrow(Params p) {
     }
   }
   // the last split of this (sequence, group) to finish merges all splits
-  if (n_splits > 1 && p.fuse_merge)
-    arrive_and_merge<D>(p, p.counters + (int64_t)b * (p.h_q / p.g) + j, &merge_last, b, j, 0,
-                        p.rows, n_splits, slot_base);
+  if (n_splits > 1 && p.fuse_merge) {
+#pragma unroll
+    for (int jj = j; jj < j + (PAIR ? 2 : 1); ++jj)
+      arrive_and_merge<D>(p, p.counters + (int64_t)b * (p.h_q / p.g) + jj, &merge_last, b, jj, 0,
+                          p.rows, n_splits, slot_base);
+  }
 
   // next item from the queue.  Every processed item draws one ticket, so
   // tickets 0 .. n_items - 1 are drawn in all; the draw of the last one
@@ -714,9 +797,11 @@ int launch_narrow_s(Params p, int n_items, int groups, hipStream_t stream) {
     // GTA: the groups of one (sequence, chunk) share an XCD (its L2 serves
     // their common RoPE key rows); GQA groups share nothing and are dealt
     // round-robin like any item, which balances the XCDs
-    const int gsz = KIND == GTA ? groups : 1;
+    // GTA2: a unit is a pair of plan items (two groups)
+    const int gsz = KIND == GTA ? groups : KIND == GTA2 ? groups / 2 : 1;
+    const int units = KIND == GTA2 ? n_items / 2 : n_items;
     p.row_blocks = gsz;
-    int blocks = (n_items + 8 * gsz - 1) / (8 * gsz) * 8 * gsz;
+    int blocks = (units + 8 * gsz - 1) / (8 * gsz) * 8 * gsz;
     if (p.queue && KIND == GQA && p.queue_base > 0 && p.queue_base < n_items) {
       blocks = p.queue_base;  // resident workgroups; the rest come from the queue
     } else {
@@ -731,9 +816,12 @@ int launch_narrow_s(Params p, int n_items, int groups, hipStream_t stream) {
 template <int KIND, int D, int DR, int RT>
 int launch_narrow_rt(const Params& p, int n_items, int groups, int stages, hipStream_t stream) {
   // pages of fewer than 16 tokens: per-row page ids, rings of 2 or 4 stages
-  if (p.page_shift < 4) {
-    return stages >= 4 ? launch_narrow_s<KIND, D, DR, RT, 4, true>(p, n_items, groups, stream)
-                       : launch_narrow_s<KIND, D, DR, RT, 2, true>(p, n_items, groups, stream);
+  // (GTA2 is only chosen for pages of at least 64 tokens)
+  if constexpr (KIND != GTA2) {
+    if (p.page_shift < 4) {
+      return stages >= 4 ? launch_narrow_s<KIND, D, DR, RT, 4, true>(p, n_items, groups, stream)
+                         : launch_narrow_s<KIND, D, DR, RT, 2, true>(p, n_items, groups, stream);
+    }
   }
   switch (stages) {
     case 2: return launch_narrow_s<KIND, D, DR, RT, 2>(p, n_items, groups, stream);
@@ -746,6 +834,8 @@ int launch_narrow_rt(const Params& p, int n_items, int groups, int stages, hipSt
 
 template <int KIND, int D, int DR>
 int launch_narrow(const Params& p, int n_items, int groups, int stages, hipStream_t stream) {
+  // GTA2 is only chosen for groups of at most 8 rows: a pair fills one row tile
+  if constexpr (KIND == GTA2) return launch_narrow_rt<KIND, D, DR, 1>(p, n_items, groups, stages, stream);
   const int rt = (p.rows + 15) / 16;
   if (rt <= 1) return launch_narrow_rt<KIND, D, DR, 1>(p, n_items, groups, stages, stream);
   if (rt <= 2) return launch_narrow_rt<KIND, D, DR, 2>(p, n_items, groups, stages, stream);
@@ -757,6 +847,7 @@ int launch_narrow(const Params& p, int n_items, int groups, int stages, hipStrea
 int run_narrow(int kind, int d, const Params& p, int n_items, int groups, int stages,
                hipStream_t stream) {
   if (kind == GTA) return launch_narrow<GTA, 128, 64>(p, n_items, groups, stages, stream);
+  if (kind == GTA2) return launch_narrow<GTA2, 128, 64>(p, n_items, groups, stages, stream);
   return d == 128 ? launch_narrow<GQA, 128, 0>(p, n_items, groups, stages, stream)
                   : launch_narrow<GQA, 64, 0>(p, n_items, groups, stages, stream);
 }
