@@ -52,6 +52,11 @@ SMALL = {
     "gla8_share": small("gla2", batch=3, h_q=16, groups=1, seqlen_lo=1, seqlen_hi=600,
                         max_seqlen=640),
     "mla_h16": small("mla", batch=2, h_q=16, seqlen_lo=1, seqlen_hi=400, max_seqlen=448),
+    # paired GTA groups: three pairs, and groups of 4 rows (half a row tile)
+    "gta_h6": small("gta_8k", batch=2, h_q=48, groups=6, seqlen_lo=1, seqlen_hi=700,
+                    max_seqlen=704),
+    "gta_g4": small("gta_8k", batch=3, h_q=8, groups=2, seqlen_lo=1, seqlen_hi=500,
+                    max_seqlen=512),
 }
 
 
@@ -310,7 +315,7 @@ def test_scores_far_above_first_tile(name):
     _check(w, inp, f"{name}/far", chunk_tokens=0)
 
 
-@pytest.mark.parametrize("name", ["gqa_llama8b", "gta_8k", "gla2", "mla_spec4"])
+@pytest.mark.parametrize("name", ["gqa_llama8b", "gta_8k", "gta_h6", "gla2", "mla_spec4"])
 def test_fused_merge_counters_return_to_zero(name):
     """Split rows are merged inside the streaming kernels by the last split
     workgroup of each row block, counted with wrapping counters: after every
