@@ -144,9 +144,127 @@ __global__ __launch_bounds__(256) void proj_kernel(ProjParams p) {
   }
 }
 
+// Streamed-weight form for K in {128, 256, 512}: a workgroup owns one head
+// and 64 input rows; each wave keeps its 16 rows' K values in registers (the
+// B operand) and the head's weights stream through LDS in blocks of 64
+// output columns (double-buffered, filled by direct-to-LDS loads), so every
+// weight byte reaches a workgroup once and the inputs are read once.  In
+// LDS, the 16-byte chunk c of weight row r sits at position c ^ (r mod 16):
+// the 16 lanes that read chunk c of rows r .. r + 15 then hit distinct banks.
+// (Keeping all output columns in registers with a deeper ring measured no
+// faster for 128 rows and slower for 1024: it costs occupancy.)
+constexpr int kColsBlk = 64;
+
+__device__ __forceinline__ void dma16w(uint64_t addr, uint32_t lds) {
+  const uint32_t l = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(addr), "s"(l)
+               : "memory");
+}
+
+template <int K>
+__global__ __launch_bounds__(256) void proj_stream_kernel(ProjParams p) {
+  constexpr int NC = K / 32;                // 32-wide k chunks
+  constexpr int RB = K * 2;                 // bytes per weight row
+  constexpr int BLK = kColsBlk * RB;        // bytes per weight block
+  constexpr int LPW = BLK / 1024 / 4;       // 1 KB loads per wave per block
+  static_assert(RB / 16 >= 16 && BLK % 4096 == 0, "rows of at least 16 chunks");
+  __shared__ __attribute__((aligned(1024))) char wbuf[2][BLK];
+
+  // block -> (head, row block): a head's row blocks sit 8 blocks apart on one
+  // XCD, which reads the head's weights from HBM once
+  const int bid = blockIdx.x;
+  const int slot = bid >> 3;
+  const int hx = slot / p.m_tiles;
+  const int mb = slot - hx * p.m_tiles;
+  const int h = hx * 8 + (bid & 7);
+  if (h >= p.H) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i = lane & 15, kg = lane >> 4;
+
+  // this wave's 16 input rows, k elements 8 kg .. 8 kg + 7 of every chunk
+  const int m = mb * kTileM + wave * 16 + i;
+  const bool mok = m < p.M;
+  const __bf16* arow = p.a + (int64_t)(mok ? m : 0) * p.a_tok + (int64_t)h * p.a_head + 8 * kg;
+  const bf16x8_t zero = {};
+  bf16x8_t areg[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+    areg[c] = mok ? *reinterpret_cast<const bf16x8_t*>(arow + 32 * c) : zero;
+
+  // weight block nb (rows 64 nb .. 64 nb + 63) into buffer `buf`: this
+  // wave's loads cover LDS bytes [1024 (LPW wave + q), + 1024) of the block
+  const char* wbase = reinterpret_cast<const char*>(p.w + (int64_t)h * p.N * K);
+  auto issue_block = [&](int nb, int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < LPW; ++q) {
+      const int off = (wave * LPW + q) * 1024 + 16 * lane;
+      const int row = off / RB, ch = (off % RB) / 16;
+      const uint64_t src = reinterpret_cast<uint64_t>(wbase) +
+                           (uint64_t)((int64_t)(nb * kColsBlk + row) * RB + (ch ^ (row & 15)) * 16);
+      dma16w(src, lds_u32(&wbuf[buf][(wave * LPW + q) * 1024]));
+    }
+  };
+
+  const int n_blocks = p.N / kColsBlk;
+  issue_block(0, 0);
+  for (int nb = 0; nb < n_blocks; ++nb) {
+    const int buf = nb & 1;
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of block nb (and older ones)
+    __syncthreads();                // every wave's part landed; buffer buf ^ 1 is free
+    if (nb + 1 < n_blocks) issue_block(nb + 1, buf ^ 1);
+    // C^T tiles: A operand = weight rows 16 t + i of the block, chunk c
+    f32x4 acc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const char* wb = wbuf[buf];
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const bf16x8_t wv = *reinterpret_cast<const bf16x8_t*>(
+            wb + (16 * t + i) * RB + (((4 * c + kg) ^ i) * 16));
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wv, areg[c], acc[t], 0, 0, 0);
+      }
+    // acc[t]: lane holds C[m][64 nb + 16 t + 4 kg + e], e < 4
+    if (mok) {
+      __bf16* crow = p.c + (int64_t)m * p.c_tok + (int64_t)h * p.c_head + nb * kColsBlk + 4 * kg;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        __bf16 v4[4] = {(__bf16)acc[t][0], (__bf16)acc[t][1], (__bf16)acc[t][2], (__bf16)acc[t][3]};
+        *reinterpret_cast<uint2*>(crow + 16 * t) = __builtin_bit_cast(uint2, v4);
+      }
+    }
+  }
+
+  // the RoPE parts of this workgroup's rows behind the product columns
+  if (p.r) {
+    const int units = p.d_r / 8;  // 16-byte units per row
+    for (int x = threadIdx.x; x < kTileM * units; x += blockDim.x) {
+      const int row = x / units, uu = x - row * units;
+      const int mm = mb * kTileM + row;
+      if (mm >= p.M) continue;
+      *reinterpret_cast<uint4*>(p.c + (int64_t)mm * p.c_tok + (int64_t)h * p.c_head + p.N + 8 * uu) =
+          *reinterpret_cast<const uint4*>(p.r + (int64_t)mm * p.r_tok + (int64_t)h * p.r_head +
+                                          8 * uu);
+    }
+  }
+}
+
 bool aligned16(const void* q) { return ((uintptr_t)q & 15u) == 0; }
 
 int launch_proj(const ProjParams& p, hipStream_t stream) {
+  if (p.K == 128 || p.K == 256 || p.K == 512) {
+    const int64_t sblocks = (int64_t)(p.H + 7) / 8 * 8 * p.m_tiles;
+    if (sblocks > INT32_MAX) return ATTN_ERR_INVALID_ARG;
+    const dim3 grid((unsigned)sblocks), block(256);
+    if (p.K == 128)
+      hipLaunchKernelGGL(proj_stream_kernel<128>, grid, block, 0, stream, p);
+    else if (p.K == 256)
+      hipLaunchKernelGGL(proj_stream_kernel<256>, grid, block, 0, stream, p);
+    else
+      hipLaunchKernelGGL(proj_stream_kernel<512>, grid, block, 0, stream, p);
+    return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+  }
   const int64_t blocks = (int64_t)(p.H + 7) / 8 * 8 * p.n_tiles * p.m_tiles;
   if (blocks > INT32_MAX) return ATTN_ERR_INVALID_ARG;
   if (p.K > 32 * KG)
