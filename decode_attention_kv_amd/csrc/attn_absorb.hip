@@ -9,14 +9,13 @@
 // o = W_UV[h] o_lat.  Both are per-head products with few rows (the step's
 // tokens) against a weight matrix per head:
 //   C[m][h][n] = sum_k A[m][h][k] * W[h][n][k]
-// with the weights stored K-contiguous ([h][n][k]), so both MFMA operands
-// load from global memory as 16-byte rows: no LDS and no transposes.
-//
-// A workgroup of four waves computes a 64 x 64 tile of one head (2 x 2 waves
-// of 32 x 32, four 16 x 16 MFMA tiles each), forming C^T = W A^T so that each
-// lane ends with four consecutive output columns of one row (one 8-byte
-// store).  All tiles of one head run on one XCD, which then reads the head's
-// weights and inputs from HBM once and serves the rest from its L2.
+// with the weights stored K-contiguous ([h][n][k]), so MFMA operands load as
+// 16-byte rows and need no transposes.  Both forms below compute C^T = W A^T
+// so that each lane ends with four consecutive output columns of one row
+// (one 8-byte store), and keep all work of one head on one XCD, which reads
+// the head's weights from HBM once.  K in {128, 256, 512}: the weights
+// stream through LDS (proj_stream_kernel); other K: 64 x 64 output tiles with
+// both operands straight from global memory (proj_kernel).
 #include "attn_device.h"
 
 namespace attn_dev {
@@ -40,6 +39,8 @@ constexpr int kTileM = 64, kTileN = 64;
 // per chunk).  K <= 32 KG takes a single group and no second buffer.
 constexpr int KG = 4;
 
+// Register-only form: a 4-wave workgroup computes a 64 x 64 output tile of
+// one head (2 x 2 waves of 32 x 32, four 16 x 16 MFMA tiles each).
 template <bool DB>
 __global__ __launch_bounds__(256) void proj_kernel(ProjParams p) {
   // block -> (head, column tile, row tile): heads are dealt to the XCDs
