@@ -121,8 +121,17 @@ inline KernelChoice choose_kernel(const attn_shape_t& sh) {
     const int lds = k.stages * narrow_stage_bytes(sh.kind, sh.head_dim, sh.d_rope) + 2048;
     int w = 163840 / lds;
     k.wgs_per_cu = w < 1 ? 1 : w > 2 ? 2 : w;
-    // more than 32 rows (four row tiles per wave): one wave per SIMD
-    if (k.rows > 32) k.wgs_per_cu = 1;
+    // more than 32 rows (four row tiles per wave): one wave per SIMD, and on
+    // pages of 16 tokens or more a shallower ring, which frees registers for
+    // the row tiles (GTA: 2 stages, measured +6 % over 5 at q_len 8; GQA
+    // with 128-wide heads: 3, +1.5 % over 4; 64-wide heads keep 6)
+    if (k.rows > 32) {
+      k.wgs_per_cu = 1;
+      if (sh.page_size >= 16 && env_stages() == 0) {
+        if (sh.kind == ATTN_KIND_GTA) k.stages = 2;
+        else if (sh.head_dim == 128 && k.stages > 3) k.stages = 3;
+      }
+    }
     // GTA groups read the same RoPE key rows: keep them on one XCD's L2
     k.same_xcd_groups = sh.kind == ATTN_KIND_GTA;
     // GTA with an even number of groups of at most 8 rows on pages of at

@@ -52,6 +52,20 @@ SMALL = {
     "gla8_share": small("gla2", batch=3, h_q=16, groups=1, seqlen_lo=1, seqlen_hi=600,
                         max_seqlen=640),
     "mla_h16": small("mla", batch=2, h_q=16, seqlen_lo=1, seqlen_hi=400, max_seqlen=448),
+    # 33-64 rows per group (four row tiles per wave): full, ragged (48, 40
+    # rows), head dim 64, single-token-row pages; past 64 rows: the general kernel
+    "gqa4_q8": small("gqa4_8k", batch=2, q_len=8, causal=True, seqlen_lo=8, seqlen_hi=400,
+                     max_seqlen=448),
+    "gta_q6": small("gta_8k", batch=2, q_len=6, causal=True, seqlen_lo=6, seqlen_hi=400,
+                    max_seqlen=448),
+    "gqa_q10_p4": small("gqa_llama8b", batch=2, q_len=10, causal=True, page_size=4,
+                        seqlen_lo=10, seqlen_hi=300, max_seqlen=320),
+    "gqa_d64_q16": small("gqa_llama8b", batch=2, head_dim=64, q_len=16, causal=True,
+                         seqlen_lo=16, seqlen_hi=300, max_seqlen=320, softmax_scale=0.125),
+    "gta_q8_p1": small("gta_8k", batch=2, q_len=8, causal=True, page_size=1, seqlen_lo=8,
+                       seqlen_hi=200, max_seqlen=200),
+    "gqa4_q12": small("gqa4_8k", batch=2, q_len=12, causal=True, seqlen_lo=12,
+                      seqlen_hi=300, max_seqlen=320),
     # paired GTA groups: three pairs, and groups of 4 rows (half a row tile)
     "gta_h6": small("gta_8k", batch=2, h_q=48, groups=6, seqlen_lo=1, seqlen_hi=700,
                     max_seqlen=704),
