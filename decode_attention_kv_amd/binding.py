@@ -205,6 +205,9 @@ def paged_kv(pool0, pool1, rope, page_table, seqlens) -> PagedKV:
 
     if pool0.stride(-1) != 1 or (pool1 is not None and pool1.stride(-1) != 1):
         raise ValueError("pool rows must be contiguous")
+    # the descriptor holds one set of strides for pool0 and pool1
+    if pool1 is not None and (pool1.shape != pool0.shape or pool1.stride() != pool0.stride()):
+        raise ValueError("pool1 must have pool0's shape and strides")
     kv = PagedKV()
     kv.pool0, kv.pool1, kv.rope_pool = _ptr(pool0), _ptr(pool1), _ptr(rope)
     kv.page_table, kv.seqlens = page_table.data_ptr(), seqlens.data_ptr()

@@ -230,6 +230,13 @@ attn_internal::KernelChoice choice_for(const attn_paged_kv_t* kv, attn_kind_t ki
   return attn_internal::choose_kernel(sh);
 }
 
+// The GQA/GTA streaming kernel keeps each lane's byte offset within a
+// 16-row slice of bf16 rows in 32 bits; larger token strides take the
+// general kernel, which addresses in 64 bits.
+bool slice_offsets_fit(int64_t token_stride) {
+  return 16 * 2 * token_stride < (1LL << 32);
+}
+
 template <int KIND, typename T, int W0, int DR>
 int run(const Params& p, const attn_plan_t* plan, int flags, hipStream_t stream) {
   int st = run_general(KIND, std::is_same<T, __bf16>::value, W0, p, plan->n_items, stream);
@@ -266,7 +273,7 @@ int attn_decode_gqa(const attn_paged_kv_t* kv, const void* q, void* out, float* 
   fill_common(p, kv, q, out, lse, q_len, h_q, h_kv, softmax_scale, flags, plan, ws, d);
   const attn_internal::KernelChoice kc =
       choice_for(kv, ATTN_KIND_GQA, q_len, h_q, h_kv, d, 0, flags);
-  if (kc.narrow) {
+  if (kc.narrow && slice_offsets_fit(kv->token_stride)) {
     // the streaming kernel merges split rows itself when the plan carries
     // counters (and the merge is not deferred); otherwise a merge launch
     p.fuse_merge = (!(flags & ATTN_DEFER_MERGE) && plan->counters) ? 1 : 0;
@@ -297,7 +304,8 @@ int attn_decode_gta(const attn_paged_kv_t* kv, const void* q, void* out, float* 
   if (rope_theta > 0.f) rope_table(p, d_rope, rope_theta);
   const attn_internal::KernelChoice kc =
       choice_for(kv, ATTN_KIND_GTA, q_len, h_q, h_kv, d, d_rope, flags);
-  if (kc.narrow) {
+  if (kc.narrow && slice_offsets_fit(kv->token_stride) &&
+      slice_offsets_fit(kv->rope_token_stride)) {
     p.fuse_merge = (!(flags & ATTN_DEFER_MERGE) && plan->counters) ? 1 : 0;
     st = run_narrow(kc.pair == 2 ? GTA2 : GTA, d, p, plan->n_items, h_kv, kc.stages, stream);
     if (st != ATTN_OK || (flags & ATTN_DEFER_MERGE) || p.fuse_merge) return st;

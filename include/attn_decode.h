@@ -218,7 +218,7 @@ size_t attn_decode_workspace_size(const attn_plan_t* plan, int h_q, int d_v);
 
 /*
  * Number of uint32 merge counters (plan->counters) a call with this plan
- * and h_q uses: batch * groups * ceil(rows / 64), rows = (h_q / groups) *
+ * and h_q uses: batch * groups * ceil(rows / 32), rows = (h_q / groups) *
  * q_len.  Returns 0 for an invalid plan.
  */
 size_t attn_decode_counter_count(const attn_plan_t* plan, int h_q);
@@ -335,9 +335,9 @@ int attn_kv_append(const attn_paged_kv_t* kv, int q_len, int heads, int width, c
  * Results are rounded to bf16 once.  Requirements: d_nope and (for the
  * output projection) d_c multiples of 32; d_c (absorb) and d_v multiples
  * of 64; d_rope a multiple of 8; every pointer 16-byte aligned; n_tok = 0
- * enqueues nothing and accepts NULL buffers.  The caller owns every buffer; outputs must not alias
- * inputs.  Returns ATTN_OK once enqueued on `stream`, INVALID_ARG (nothing
- * enqueued) for inconsistent arguments.
+ * enqueues nothing and accepts NULL buffers.  The caller owns every buffer;
+ * outputs must not alias inputs.  Returns ATTN_OK once enqueued on `stream`,
+ * INVALID_ARG (nothing enqueued) for inconsistent arguments.
  */
 int attn_latent_absorb_query(const void* q_nope, const void* q_rope, const void* w_uk,
                              void* q_out, int n_tok, int h_q, int d_nope, int d_c, int d_rope,

@@ -217,6 +217,27 @@ def test_paged_kv_check():
     assert binding.attn_paged_kv_check(kv) == binding.ATTN_ERR_INVALID_ARG
 
 
+def test_paged_kv_needs_one_layout_for_both_pools():
+    """The descriptor has one set of strides: a V pool laid out differently
+    from the K pool is refused rather than read with the K pool's strides."""
+    import torch
+
+    table = torch.zeros((2, 3), dtype=torch.int32)
+    seqlens = torch.tensor([5, 9], dtype=torch.int32)
+    k = torch.zeros((4, 16, 2, 64), dtype=torch.bfloat16)
+    kv = binding.paged_kv(k, torch.zeros_like(k), None, table, seqlens)
+    assert (kv.page_stride, kv.token_stride, kv.head_stride) == (16 * 2 * 64, 2 * 64, 64)
+    head_major = torch.zeros((4, 2, 16, 64), dtype=torch.bfloat16).permute(0, 2, 1, 3)
+    with pytest.raises(ValueError):
+        binding.paged_kv(k, head_major, None, table, seqlens)
+    with pytest.raises(ValueError):
+        binding.paged_kv(k, torch.zeros((4, 16, 2, 32), dtype=torch.bfloat16), None, table, seqlens)
+    # the same non-default layout for both pools is fine
+    kv = binding.paged_kv(head_major, head_major.clone(memory_format=torch.preserve_format),
+                          None, table, seqlens)
+    assert kv.token_stride == 64 and kv.head_stride == 16 * 64
+
+
 def _fake_call(kind="gqa", **over):
     """A decode call with fake (never dereferenced) aligned device pointers:
     validation must reject it before any launch."""

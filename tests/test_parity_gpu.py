@@ -139,6 +139,41 @@ def test_small_pages_head_major_and_nan_tails(name, page_size):
     H.compare(H.to_np(out), H.to_np(lse), ref, ref_lse, H.value_max(w, inp), f"{name}/hnd/P{page_size}")
 
 
+def _slot_major(t, n_pages):
+    """t's pages as the first pages of a slot-major pool [slot][n_pages][heads]
+    [width] (token stride n_pages * heads * width elements)."""
+    P, Hh, Wd = t.shape[1:]
+    big = torch.empty((P, n_pages, Hh, Wd), dtype=t.dtype, device=t.device)
+    view = big.permute(1, 0, 2, 3)
+    view[: t.shape[0]] = t
+    return view
+
+
+# (workload, page size, token stride in bytes to reach): a 16-row slice's
+# per-lane offsets of the GQA/GTA streaming kernel pass 2^32 bytes, a 64-row
+# tile's offsets of the latent one 2^31; both then take the general kernel
+@pytest.mark.parametrize("name,page_size,stride_bytes", [("gqa_llama8b", 16, 2 ** 32 // 15),
+                                                          ("gta_8k", 16, 2 ** 32 // 15),
+                                                          ("mla", 64, 2 ** 31 // 63)])
+def test_token_strides_past_32_bit_offsets(name, page_size, stride_bytes):
+    w = SMALL[name].with_(page_size=page_size)
+    print(f"[stride] {name} P={page_size}", flush=True)
+    inp = synth.make_inputs(w)
+    d = H.to_device(w, inp)
+    row = d["pool0"].shape[2] * d["pool0"].shape[3] * 2
+    n_pages = -(-stride_bytes // row) + 1
+    assert n_pages * row > stride_bytes and n_pages >= d["pool0"].shape[0]
+    d["pool0"] = _slot_major(d["pool0"], n_pages)
+    if d["pool1"] is not None:
+        d["pool1"] = _slot_major(d["pool1"], n_pages)
+    out, lse, _ = H.run(w, d, chunk_tokens=128)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.decode(w, inp)
+    H.compare(H.to_np(out), H.to_np(lse), ref, ref_lse, H.value_max(w, inp), f"{name}/stride")
+    del d
+    torch.cuda.empty_cache()
+
+
 def test_empty_and_single_token_sequences():
     w = SMALL["gqa_llama8b"]
     inp = synth.make_inputs(w, seqlens=np.array([0, 1, 65, 0], dtype=np.int32))
