@@ -66,6 +66,16 @@ SMALL = {
                        seqlen_hi=200, max_seqlen=200),
     "gqa4_q12": small("gqa4_8k", batch=2, q_len=12, causal=True, seqlen_lo=12,
                       seqlen_hi=300, max_seqlen=320),
+    # latent groups whose rows are no multiple of 16: 24 rows (one partial
+    # row tile), 60 (two row tiles, the last partial), 144 (row blocks of
+    # 64, 64 and 16), and 3 rows in each of four GLA groups
+    "mla_h24": small("mla", batch=3, h_q=24, seqlen_lo=1, seqlen_hi=500, max_seqlen=512),
+    "gla2_h40_q3": small("gla2", batch=2, h_q=40, q_len=3, causal=True, seqlen_lo=3,
+                         seqlen_hi=400, max_seqlen=448),
+    "mla_h72_q2": small("mla", batch=2, h_q=72, q_len=2, causal=True, seqlen_lo=2,
+                        seqlen_hi=300, max_seqlen=320),
+    "gla4_h12": small("gla2", batch=3, h_q=12, groups=4, seqlen_lo=1, seqlen_hi=400,
+                      max_seqlen=448),
     # paired GTA groups: three pairs, and groups of 4 rows (half a row tile)
     "gta_h6": small("gta_8k", batch=2, h_q=48, groups=6, seqlen_lo=1, seqlen_hi=700,
                     max_seqlen=704),
@@ -364,7 +374,8 @@ def test_scores_far_above_first_tile(name):
     _check(w, inp, f"{name}/far", chunk_tokens=0)
 
 
-@pytest.mark.parametrize("name", ["gqa_llama8b", "gta_8k", "gta_h6", "gla2", "mla_spec4"])
+@pytest.mark.parametrize("name", ["gqa_llama8b", "gta_8k", "gta_h6", "gla2", "mla_spec4", "gqa4_q8",
+                                  "gla2_h40_q3", "mla_h72_q2"])
 def test_fused_merge_counters_return_to_zero(name):
     """Split rows are merged inside the streaming kernels by the last split
     workgroup of each row block, counted with wrapping counters: after every
