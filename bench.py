@@ -200,8 +200,10 @@ def main():
                          "the decode and projects the latent output to 128 per head after it "
                          "(attn_latent_absorb_query / attn_latent_project_output, random "
                          "weights)")
-    ap.add_argument("--queue", choices=["on", "off"], default="off",
-                    help="on: the GQA kernel hands items out through a work-queue counter")
+    ap.add_argument("--queue", choices=["auto", "on", "off"], default="auto",
+                    help="on: the GQA kernel hands items out through a work-queue counter; "
+                         "auto (default): on for GQA pages under 16 tokens, where it measured "
+                         "faster on ragged lengths (slower on larger pages)")
     ap.add_argument("--set", action="append", default=[], metavar="FIELD=VALUE",
                     help="override a workload field (e.g. q_len=2, h_q=16, groups=1, "
                          "page_size=1, batch=64); the result is then not the named workload")
@@ -269,7 +271,9 @@ def main():
     dev_buf = torch.zeros((B + max_items, 4), dtype=torch.int32, device=dev)
     counters = None  # merge counters (zero-filled once), sized from the first plan
     placement = [None]  # where the last plan went: inline / device / host
-    queue = torch.zeros(1, dtype=torch.int32, device=dev) if args.queue == "on" else None
+    use_queue = args.queue == "on" or (args.queue == "auto" and w.kind == "gqa" and
+                                       w.page_size < 16)
+    queue = torch.zeros(1, dtype=torch.int32, device=dev) if use_queue else None
 
     def make_plan(k):
         i = k % 2
@@ -466,7 +470,7 @@ def main():
                        "kv_bytes_per_step": int(kvb), "gpus": 1, "layout": args.layout,
                        "cache_flush": args.flush, "plan_mem": placement[0],
                        "with_append": bool(args.with_append),
-                       "with_absorb": bool(args.with_absorb), "queue": args.queue,
+                       "with_absorb": bool(args.with_absorb), "queue": "on" if use_queue else "off",
                        "merge": args.merge},
             "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
             "tokens_per_s": round(tokens / (ms * 1e-3), 1),
