@@ -184,6 +184,55 @@ def test_token_strides_past_32_bit_offsets(name, page_size, stride_bytes):
     torch.cuda.empty_cache()
 
 
+def _random_cases(n=30, seed=2026):
+    """Seeded random shapes inside the supported envelope (the same list on
+    every run): kind, head and latent widths, group counts and sizes, q_len,
+    page size, lengths, chunk length and pool layout."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        kind = ("gqa", "gta", "latent")[i % 3]
+        q_len = int(rng.choice([1, 1, 2, 3, 5, 8]))
+        if kind == "gqa":
+            d = int(rng.choice([64, 128]))
+            groups, g = int(rng.choice([1, 2, 4, 8])), int(rng.choice([1, 2, 3, 4, 5, 8, 16]))
+            base = W["gqa_llama8b"].with_(head_dim=d, softmax_scale=d ** -0.5,
+                                          dtype="fp32" if rng.random() < 0.2 else "bf16")
+        elif kind == "gta":
+            groups, g = int(rng.choice([1, 2, 4, 6])), int(rng.choice([1, 2, 4, 5, 8]))
+            base = W["gta_8k"]
+        else:
+            d = int(rng.choice([256, 512]))
+            groups, g = int(rng.choice([1, 2, 4])), int(rng.choice([1, 3, 8, 16, 32, 48]))
+            base = W["gla2"].with_(head_dim=d, softmax_scale=(d + 64) ** -0.5)
+        page = int(rng.choice([1, 2, 4, 8, 16, 32, 64, 128]))
+        hi = int(rng.integers(q_len + 1, 700))
+        w = base.with_(name=f"rand{i}", batch=int(rng.integers(1, 5)), q_len=q_len,
+                       causal=q_len > 1, h_q=groups * g, groups=groups, page_size=page,
+                       seqlen_lo=q_len, seqlen_hi=hi, max_seqlen=hi + int(rng.integers(0, 64)),
+                       permute_pages=True, seed=1000 + i)
+        out.append((w, int(rng.choice([0, 64, 128, 192])), bool(rng.random() < 0.3)))
+    return out
+
+
+RANDOM_CASES = _random_cases()
+
+
+@pytest.mark.parametrize("case", range(len(RANDOM_CASES)))
+def test_random_shapes(case):
+    w, chunk, head_major = RANDOM_CASES[case]
+    print(f"[random] {w.name} {w.kind} {w.dtype} d={w.head_dim} G={w.groups} h_q={w.h_q} "
+          f"T={w.q_len} P={w.page_size} chunk={chunk} head_major={head_major}", flush=True)
+    inp = synth.make_inputs(w)
+    d = H.to_device(w, inp)
+    if head_major:
+        d = _head_major(d)
+    out, lse, _ = H.run(w, d, chunk_tokens=chunk)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.decode(w, inp)
+    H.compare(H.to_np(out), H.to_np(lse), ref, ref_lse, H.value_max(w, inp), w.name)
+
+
 def test_empty_and_single_token_sequences():
     w = SMALL["gqa_llama8b"]
     inp = synth.make_inputs(w, seqlens=np.array([0, 1, 65, 0], dtype=np.int32))
