@@ -184,7 +184,7 @@ def test_token_strides_past_32_bit_offsets(name, page_size, stride_bytes):
     torch.cuda.empty_cache()
 
 
-def _random_cases(n=30, seed=2026):
+def _random_cases(n=60, seed=2026):
     """Seeded random shapes inside the supported envelope (the same list on
     every run): kind, head and latent widths, group counts and sizes, q_len,
     page size, lengths, chunk length and pool layout."""
