@@ -109,3 +109,38 @@ def test_absorb_decode_project_chain(wl):
     got = out.float().cpu().numpy()
     rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
     assert rel <= H.REL_L2, f"{wl}: chain rel-L2 {rel:.3e}"
+
+
+def _random_shapes(n=20, seed=77):
+    """Seeded shapes inside the documented limits: both projections, the
+    streamed-weight form (K of 128, 256, 512) and the register-only one."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        out.append((int(rng.integers(1, 300)), int(rng.choice([1, 2, 3, 5, 8, 16, 24, 128])),
+                    int(rng.choice([32, 64, 96, 128, 192, 256])),
+                    int(rng.choice([64, 128, 192, 256, 512])), int(rng.choice([0, 8, 16, 64])),
+                    int(rng.choice([64, 128, 192, 256]))))
+    return out
+
+
+RANDOM_SHAPES = _random_shapes()
+
+
+@pytest.mark.parametrize("case", range(len(RANDOM_SHAPES)))
+def test_random_shapes(case):
+    n, hq, dn, dc, dr, dv = RANDOM_SHAPES[case]
+    print(f"[proj-random] n={n} h={hq} d_nope={dn} d_c={dc} d_rope={dr} d_v={dv}", flush=True)
+    p = synth.make_projection_inputs(n, hq, dn, dc, dr, dv, seed=300 + case)
+    got = binding.absorb_query(_dev(p["q_nope"]), _dev(p["q_rope"]), _dev(p["w_uk"]))
+    out = binding.project_output(_dev(p["o_lat"]), _dev(p["w_uv"]))
+    torch.cuda.synchronize()
+    got = got.float().cpu().numpy()
+    ref = oracle.absorb_query(p["q_nope"], p["q_rope"], p["w_uk"])
+    S = oracle.absorb_query(np.abs(p["q_nope"]), None, np.abs(p["w_uk"]))
+    _check(got[:, :, :dc], ref[:, :, :dc], S, dn, f"random {case} latent")
+    if dr:
+        assert np.array_equal(got[:, :, dc:], p["q_rope"]), f"random {case}: RoPE part"
+    ref = oracle.project_output(p["o_lat"], p["w_uv"])
+    S = oracle.project_output(np.abs(p["o_lat"]), np.abs(p["w_uv"]))
+    _check(out.float().cpu().numpy(), ref, S, dc, f"random {case} output")
