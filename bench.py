@@ -139,34 +139,121 @@ def apply_overrides(w, items):
     return w.with_(name=f"{w.name}[{tag}]", **kw)
 
 
-def cpu_baseline(w, inp, seconds):
+def value_max(w, inp, batch_index):
+    """max |V| over the values the sampled sequences attend (V pool, tied
+    state or latent), read through the page table."""
+    import numpy as np
+
+    src = inp["pool1"] if w.kind == "gqa" else inp["pool0"]
+    m = 0.0
+    for b in batch_index:
+        L = int(inp["seqlens"][b])
+        n = -(-L // w.page_size)
+        if n:
+            v = src[inp["page_table"][b, :n]].reshape(-1, src.shape[2], src.shape[3])[:L]
+            m = max(m, float(np.abs(v).max()))
+    return m or 1.0
+
+
+# parity bar for bf16 inputs with fp32 accumulation: relative L2 error of the
+# compared output <= 5e-3 and max abs error <= 1e-2 * max|V|
+REL_L2_MAX = 5e-3
+MAX_ABS_FRAC = 1e-2
+
+
+def cpu_baseline(w, inp, seconds, gpu_out=None):
     """The fp64 oracle on a bounded sample of the same batch: whole sequences
-    in batch order, repeating the batch, until about `seconds` of work."""
+    in batch order, repeating the batch, until about `seconds` of work.
+
+    With `gpu_out` (the benched step's output, [B, T, H, d_v] on the host),
+    the oracle's output for every sequence of the first pass is also compared
+    with the GPU's rows of that sequence (outside the timed oracle work)."""
     import numpy as np
 
     import oracle
 
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        threads = 1
+        blas = None
+    cores = len(os.sched_getaffinity(0))
     done, t_used = [], 0.0
+    err2 = ref2 = 0.0
+    max_abs, compared = 0.0, []
     while t_used < seconds and w.batch > 0:
         for b in range(w.batch):
             t0 = time.perf_counter()
-            oracle.decode(w, inp, batch_index=[b])
+            ref, _ = oracle.decode(w, inp, batch_index=[b])
             t_used += time.perf_counter() - t0
+            if gpu_out is not None and b not in compared:
+                e = gpu_out[b].astype(np.float64) - ref[0]
+                err2 += float((e * e).sum())
+                ref2 += float((ref[0] * ref[0]).sum())
+                max_abs = max(max_abs, float(np.abs(e).max()) if e.size else 0.0)
+                compared.append(b)
             done.append(b)
             if t_used >= seconds:
                 break
     L = inp["seqlens"][done]
     kvb = oracle.kv_bytes(w, L)
     passes = len(done) / w.batch
-    return {"value": kvb / t_used / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{len(done)} sequence decodes ({passes:.2f} passes over the {w.batch}-sequence "
-                      f"batch, lengths {int(L.min())}..{int(L.max())}) in {t_used:.1f} s; "
-                      f"{len(done) * w.q_len / t_used:.1f} decode tokens/s"}
+    res = {"value": kvb / t_used / 1e9, "unit": "GB/s", "cores": cores, "blas_threads": blas,
+           "kind": "oracle",
+           "sample": f"{len(done)} sequence decodes ({passes:.2f} passes over the {w.batch}-sequence "
+                     f"batch, lengths {int(L.min())}..{int(L.max())}) in {t_used:.1f} s; "
+                     f"{len(done) * w.q_len / t_used:.1f} decode tokens/s"}
+    parity = None
+    if gpu_out is not None and compared:
+        rel = (err2 ** 0.5) / (ref2 ** 0.5) if ref2 > 0 else err2 ** 0.5
+        bound = MAX_ABS_FRAC * value_max(w, inp, compared)
+        parity = {"sequences": compared, "rel_l2": rel, "max_abs": max_abs,
+                  "rel_l2_max": REL_L2_MAX, "max_abs_max": bound,
+                  "pass": bool(rel <= REL_L2_MAX and max_abs <= bound)}
+    return res, parity
+
+
+def measure_ceilings(dev, binding, reps=5):
+    """Streaming-read and bf16 MFMA ceilings of this GPU from the library's
+    probe kernels (event-timed on the launch stream): reads of a 4 GiB
+    buffer (far past the 256 MB Infinity Cache) into registers and straight
+    into LDS, and register-only MFMA products."""
+    import torch
+
+    n = 4 << 30
+    buf = torch.ones(n // 4, dtype=torch.int32, device=dev)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    s = stream.cuda_stream
+    out = {}
+    for mode, name in ((0, "read_vgpr_nt_gbps"), (1, "read_lds_nt_gbps")):
+        best = 0.0
+        for k in range(reps + 2):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            st = binding.attn_probe_stream_read(buf.data_ptr(), n, mode, sink.data_ptr(), s)
+            e1.record(stream)
+            if st != binding.ATTN_OK:
+                raise binding.AttnError(st, "attn_probe_stream_read")
+            e1.synchronize()
+            if k >= 2:
+                best = max(best, n / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+        out[name] = round(best, 1)
+    del buf
+    best = 0.0
+    for k in range(reps + 2):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        st, fl = binding.attn_probe_mfma(20000, sink.data_ptr(), s)
+        e1.record(stream)
+        if st != binding.ATTN_OK:
+            raise binding.AttnError(st, "attn_probe_mfma")
+        e1.synchronize()
+        if k >= 2:
+            best = max(best, fl / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+    out["mfma_bf16_tflops"] = round(best, 1)
+    out["hbm_read_gbps"] = max(out["read_vgpr_nt_gbps"], out["read_lds_nt_gbps"])
+    return out
 
 
 def main():
@@ -174,7 +261,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="gqa_llama8b")
+    ap.add_argument("--workload", default="gqa_llama8b_8k",
+                    help="default: the Llama-3-8B-shaped GQA layer at 8K context")
     ap.add_argument("--flush", choices=["read", "write", "none"], default="read",
                     help="evict L2 / Infinity Cache before each timed step by reading (default) "
                          "or writing a 1 GiB buffer, outside the timed interval")
@@ -209,6 +297,11 @@ def main():
                          "page_size=1, batch=64); the result is then not the named workload")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="only measure this GPU's streaming-read and bf16 MFMA ceilings with "
+                         "the library's probe kernels and print them")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the ceiling probes after the timed steps")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -230,6 +323,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n, "launches": 3}))
+        return
+    if args.ceilings:
+        print(json.dumps(measure_ceilings(dev, binding)))
         return
 
     w = apply_overrides(synth.WORKLOADS[args.workload], args.set)
@@ -446,18 +542,40 @@ def main():
     tokens = B * T
     sha = kernel_sha(w)
 
-    # output sanity on the last step (the parity tests do the real check)
+    # the last timed step's output, kept for the comparison with the oracle
     torch.cuda.synchronize()
     assert torch.isfinite(out.float()).all().item(), "non-finite output"
+    out_host = out.float().cpu().numpy()
 
-    roofline = {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
-                "traffic": load_traffic(w.name, sha),
-                "algorithmic_bytes_per_launch": int(kvb),
-                "mfma_tflops": round(dec_tflops, 1),
-                "mfma_frac": round(dec_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                "kernel_ms_mean": round(float(dec_ms.mean()), 5),
-                "kernel_source_sha256_16": sha}
+    ceil = None
+    if not args.no_ceilings:
+        print("[bench] ceiling probes", file=sys.stderr, flush=True)
+        ceil = measure_ceilings(dev, binding)
+
+    # the dominant kernel's roof: HBM unless the bf16 matrix work takes longer
+    # at peak than the cache read (latent heads at high intensity)
+    mfma_bound = fl / (MFMA_BF16_PEAK_TFLOPS * 1e12) > kvb / (HBM_PEAK_GBPS * 1e9)
+    if mfma_bound:
+        roofline = {"bound": "mfma", "achieved": round(dec_tflops, 1),
+                    "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(dec_tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
+    else:
+        roofline = {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS,
+                    "unit": "GB/s", "frac": round(dec_gbps / HBM_PEAK_GBPS, 4)}
+    roofline.update({"traffic": load_traffic(w.name, sha),
+                     "algorithmic_bytes_per_launch": int(kvb),
+                     "algorithmic_flops_per_launch": int(fl),
+                     "hbm_gbps": round(dec_gbps, 1),
+                     "hbm_frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
+                     "mfma_tflops": round(dec_tflops, 1),
+                     "mfma_frac": round(dec_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "kernel_ms_mean": round(float(dec_ms.mean()), 5),
+                     "kernel_source_sha256_16": sha})
+    if ceil is not None:
+        roofline["measured_ceilings"] = ceil
+        roofline["frac_of_measured"] = round(
+            dec_tflops / ceil["mfma_bf16_tflops"] if mfma_bound
+            else dec_gbps / ceil["hbm_read_gbps"], 4)
 
     line = {"metric": "decode-attn KV GB/s (% of MI355X HBM peak) and tokens/s at 8K ctx",
             "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -484,10 +602,16 @@ def main():
             "plan": {"items": int(plan0.n_items), "max_splits": int(plan0.max_splits),
                      "partial_slots": int(plan0.n_partial_slots)},
             "roofline": roofline}
+    parity = None
     if not args.no_cpu_baseline:
-        print("[bench] oracle cpu baseline", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
+        print("[bench] oracle cpu baseline (and the benched output against it)", file=sys.stderr,
+              flush=True)
+        line["cpu_baseline"], parity = cpu_baseline(w, inp, args.cpu_seconds, out_host)
+        line["parity"] = parity
     print(json.dumps(line), flush=True)
+    if parity is not None and not parity["pass"]:
+        print(f"[bench] the benched output does not match the oracle: {parity}", file=sys.stderr)
+        sys.exit(3)
 
 
 if __name__ == "__main__":

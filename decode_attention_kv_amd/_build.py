@@ -3,8 +3,9 @@
 Sources: csrc/attn_host.cpp (host-only planning and checks),
 csrc/attn_decode.hip (entry points, merge kernel), one translation unit
 per decode kernel family (attn_general.hip, attn_narrow.hip,
-attn_wide.hip) and the cache append (attn_append.hip), compiled in
-parallel.  Packed-fp32 VALU ops are disabled
+attn_wide.hip), the cache append (attn_append.hip), the projections
+around the latent kernel (attn_absorb.hip) and the measurement probes
+(attn_probe.hip), compiled in parallel.  Packed-fp32 VALU ops are disabled
 for device code.
 """
 import concurrent.futures
@@ -18,7 +19,7 @@ LIB = os.path.join(PKG, "libattn_decode.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 SOURCES = ("attn_host.cpp", "attn_decode.hip", "attn_general.hip", "attn_narrow.hip",
-           "attn_wide.hip", "attn_append.hip", "attn_absorb.hip")
+           "attn_wide.hip", "attn_append.hip", "attn_absorb.hip", "attn_probe.hip")
 
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-I" + os.path.join(ROOT, "include"),

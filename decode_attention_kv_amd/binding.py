@@ -115,6 +115,10 @@ def lib():
     L.attn_latent_project_output.argtypes = [c_void_p, c_void_p, c_void_p, c_int, c_int, c_int,
                                              c_int, c_void_p]
     L.attn_latent_project_output.restype = c_int
+    L.attn_probe_stream_read.argtypes = [c_void_p, c_size_t, c_int, c_void_p, c_void_p]
+    L.attn_probe_stream_read.restype = c_int
+    L.attn_probe_mfma.argtypes = [c_int, c_void_p, POINTER(ctypes.c_double), c_void_p]
+    L.attn_probe_mfma.restype = c_int
     _lib = L
     return L
 
@@ -190,6 +194,17 @@ def attn_latent_absorb_query(q_nope, q_rope, w_uk, q_out, n_tok, h_q, d_nope, d_
 
 def attn_latent_project_output(o_lat, w_uv, out, n_tok, h_q, d_c, d_v, stream) -> int:
     return lib().attn_latent_project_output(o_lat, w_uv, out, n_tok, h_q, d_c, d_v, stream)
+
+
+def attn_probe_stream_read(buf, nbytes, mode, sink, stream) -> int:
+    return lib().attn_probe_stream_read(buf, nbytes, mode, sink, stream)
+
+
+def attn_probe_mfma(iters, sink, stream):
+    """Returns (status, FLOPs of the launch)."""
+    fl = ctypes.c_double(0.0)
+    st = lib().attn_probe_mfma(iters, sink, ctypes.byref(fl), stream)
+    return st, fl.value
 
 
 # ------------------------------------------------------------ torch plumbing

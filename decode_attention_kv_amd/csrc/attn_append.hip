@@ -23,7 +23,7 @@ struct AppendParams {
   const int32_t* page_table;
   const int32_t* seqlens;
   int64_t page_stride, token_stride, head_stride, rpage_stride, rtoken_stride;
-  int32_t q_len, heads, width, d_rope, max_pages, page_shift, rope_on;
+  int32_t q_len, heads, width, d_rope, max_pages, num_pages, page_shift, rope_on;
   float rope_hi[kMaxRope / 2];
   float rope_lo[kMaxRope / 2];
 };
@@ -34,8 +34,11 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams a) {
   const int bt = blockIdx.x;
   const int b = bt / a.q_len, t = bt - b * a.q_len;
   const int pos = a.seqlens[b] - a.q_len + t;
-  if (pos < 0) return;
+  // a position before the cache start, past the sequence's page-table row,
+  // or on a page id outside the pools is skipped: nothing is written
+  if (pos < 0 || (pos >> a.page_shift) >= a.max_pages) return;
   const int64_t page = a.page_table[(int64_t)b * a.max_pages + (pos >> a.page_shift)];
+  if (page < 0 || page >= a.num_pages) return;
   const int64_t slot = pos & ((1 << a.page_shift) - 1);
   const int upr = a.width * (int)sizeof(T) / 16;  // 16-byte units per head row
   for (int u = threadIdx.x; u < a.heads * upr; u += blockDim.x) {
@@ -79,7 +82,8 @@ extern "C" int attn_kv_append(const attn_paged_kv_t* kv, int q_len, int heads, i
                               const void* new0, const void* new1, int d_rope, const void* new_rope,
                               float rope_theta, hipStream_t stream) {
   if (!kv || !kv->pool0 || !kv->page_table || !kv->seqlens || !new0) return ATTN_ERR_INVALID_ARG;
-  if (kv->batch <= 0 || q_len < 1 || heads < 1 || width < 1 || kv->max_pages_per_seq <= 0)
+  if (kv->batch <= 0 || q_len < 1 || heads < 1 || width < 1 || kv->max_pages_per_seq <= 0 ||
+      kv->num_pages <= 0)
     return ATTN_ERR_INVALID_ARG;
   if (kv->dtype != ATTN_BF16 && kv->dtype != ATTN_FP32) return ATTN_ERR_INVALID_ARG;
   const int P = kv->page_size;
@@ -115,6 +119,7 @@ extern "C" int attn_kv_append(const attn_paged_kv_t* kv, int q_len, int heads, i
   a.width = width;
   a.d_rope = new_rope ? d_rope : 0;
   a.max_pages = kv->max_pages_per_seq;
+  a.num_pages = kv->num_pages;
   int shift = 0;
   while ((1 << shift) < P) ++shift;
   a.page_shift = shift;

@@ -123,6 +123,33 @@ int ilog2_pow2(int v) {
   return s;
 }
 
+// The decode kernels take every sequence's length, split count and chunk
+// from the plan (its device arrays are copies of the host arrays, or the
+// host arrays travel in the launch arguments), not from kv->seqlens.  So the
+// host arrays are checked before any launch: every length fits the page
+// table's row (capacity = max_pages_per_seq * page_size) and, for causal
+// calls, holds at least q_len keys; the chunks cover it; split partial
+// slots stay inside the plan's count; every item names a real sequence,
+// group and split with its chunk's first token.
+int check_plan(const attn_plan_t* plan, int64_t capacity, int min_len) {
+  if (!plan->seqinfo_host || !plan->items_host) return ATTN_ERR_INVALID_ARG;
+  for (int b = 0; b < plan->batch; ++b) {
+    const int32_t* si = plan->seqinfo_host + 4 * (int64_t)b;
+    const int64_t n = si[0], base = si[1], L = si[2], chunk = si[3];
+    if (n < 1 || L < 0 || L > capacity || L < min_len || chunk <= 0 || n * chunk < L)
+      return ATTN_ERR_INVALID_ARG;
+    if (n > 1 && (base < 0 || base + n > plan->n_partial_slots)) return ATTN_ERR_INVALID_ARG;
+  }
+  for (int64_t k = 0; k < plan->n_items; ++k) {
+    const int32_t* it = plan->items_host + 4 * k;
+    if (it[0] < 0 || it[0] >= plan->batch || it[1] != k % plan->n_groups) return ATTN_ERR_INVALID_ARG;
+    const int32_t* si = plan->seqinfo_host + 4 * (int64_t)it[0];
+    if (it[2] < 0 || it[2] >= si[0] || (int64_t)it[3] != (int64_t)it[2] * si[3])
+      return ATTN_ERR_INVALID_ARG;
+  }
+  return ATTN_OK;
+}
+
 int validate(const attn_paged_kv_t* kv, const void* q, const void* out, int q_len, int h_q,
              int groups, int flags, const attn_plan_t* plan, const void* ws, size_t ws_bytes, int d_v,
              bool need_pool1, bool need_rope) {
@@ -153,6 +180,9 @@ int validate(const attn_paged_kv_t* kv, const void* q, const void* out, int q_le
       return ATTN_ERR_INVALID_ARG;
     if (kv->rope_token_stride < 0 || kv->rope_page_stride < 0) return ATTN_ERR_INVALID_ARG;
   }
+  const int pst = check_plan(plan, (int64_t)kv->max_pages_per_seq * kv->page_size,
+                             (flags & ATTN_CAUSAL) && q_len > 1 ? q_len : 0);
+  if (pst != ATTN_OK) return pst;
   const size_t need = attn_decode_workspace_size(plan, h_q, d_v);
   if (need > 0 && (!ws || ws_bytes < need || ((uintptr_t)ws & 255u)))
     return ATTN_ERR_WORKSPACE;
@@ -342,11 +372,13 @@ int attn_decode_latent(const attn_paged_kv_t* kv, const void* q, void* out, floa
 
 int attn_decode_merge(const attn_plan_t* plan, int h_q, int d_v, attn_dtype_t dtype,
                       const void* ws, size_t ws_bytes, void* out, float* lse, hipStream_t stream) {
-  if (!plan || !out || h_q <= 0 || plan->q_len <= 0 || plan->batch <= 0)
+  if (!plan || !out || h_q <= 0 || plan->q_len <= 0 || plan->batch <= 0 || plan->n_groups <= 0)
     return ATTN_ERR_INVALID_ARG;
   if (!plan_on_device(plan) && !plan_inline(plan)) return ATTN_ERR_INVALID_ARG;
   if (dtype != ATTN_BF16 && dtype != ATTN_FP32) return ATTN_ERR_INVALID_ARG;
   if (d_v != 64 && d_v != 128 && d_v != 256 && d_v != 512) return ATTN_ERR_UNSUPPORTED;
+  if (h_q % plan->n_groups) return ATTN_ERR_INVALID_ARG;
+  if (check_plan(plan, INT64_MAX, 0) != ATTN_OK) return ATTN_ERR_INVALID_ARG;
   if (plan->n_partial_slots <= 0) return ATTN_OK;
   const size_t need = attn_decode_workspace_size(plan, h_q, d_v);
   if (!ws || ws_bytes < need || ((uintptr_t)ws & 255u)) return ATTN_ERR_WORKSPACE;

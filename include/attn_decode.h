@@ -93,6 +93,10 @@ enum {
  *             sequence uses are in [0, num_pages); the rest may be -1 and are
  *             never read.
  *   seqlens   int32 [batch], 0 <= seqlens[b] <= max_pages_per_seq*page_size.
+ *             Read only by attn_kv_append: the decode calls take every
+ *             sequence's length from the plan (attn_decode_plan's
+ *             seqlens_host), so a plan must be made from the lengths the
+ *             cache holds when the decode runs.
  *
  * Requirements: page_size is a power of two; pool base pointers and every
  * row start are 16-byte aligned (strides * element size multiple of 16).
@@ -116,9 +120,17 @@ typedef struct {
 
 /*
  * Split plan: which (sequence, group, token chunk) each workgroup handles.
- * Filled on the host by attn_decode_plan; the caller copies the two host
- * arrays to device memory and stores the device pointers in `items` and
- * `seqinfo` before the decode call.
+ * Filled on the host by attn_decode_plan.  The kernels read it either from
+ * device copies of the two host arrays (the caller copies them and stores
+ * the device pointers in `items` and `seqinfo`) or, when `inline_ok` is set
+ * and both pointers are left NULL, from the launch arguments, packed by the
+ * call from the host arrays (see "Launch-argument plans" below: no copy is
+ * needed).  Either way the host arrays must still hold what
+ * attn_decode_plan wrote when a decode or merge call is made: every call
+ * checks them on the host (each length at most max_pages_per_seq *
+ * page_size, at least q_len for causal calls; chunks, splits, partial slots
+ * and items consistent) and returns INVALID_ARG, launching nothing, if they
+ * are not.  Device copies must equal the host arrays.
  *
  *   items   [n_items][4]  int32: b, group j, split index s, first token t0
  *           (the chunk is [t0, min(t0 + chunk, L_b)))
@@ -202,7 +214,10 @@ int attn_decode_plan_max_items(int batch, int n_groups, int max_seqlen);
  * Errors: INVALID_ARG for null pointers, non-positive sizes, negative
  * lengths, causal lengths below q_len, chunk_tokens not a multiple of 64;
  * WORKSPACE if max_items is too small.  On success plan->items and
- * plan->seqinfo are NULL; the caller sets them to the device copies.
+ * plan->seqinfo are NULL: the caller sets them to device copies of the host
+ * arrays, or, when plan->inline_ok is 1, may leave them NULL so that the
+ * calls pass the plan in the kernels' launch arguments.  The host arrays
+ * must outlive every call made with the plan.
  */
 int attn_decode_plan(const attn_shape_t* shape, const int32_t* seqlens_host, int cu_count,
                      int chunk_tokens, int32_t* items_host, int32_t* seqinfo_host,
@@ -230,8 +245,8 @@ size_t attn_decode_counter_count(const attn_plan_t* plan, int h_q);
  *   lse  [batch][q_len][h_q] fp32, or NULL
  *   flags ATTN_CAUSAL and/or ATTN_DEFER_MERGE
  *   plan, workspace  from attn_decode_plan / attn_decode_workspace_size;
- *        the workspace must be 256-byte aligned (may be NULL if the plan
- *        splits nothing and the kernel needs no flags)
+ *        the workspace is always required (its size is at least 256 bytes)
+ *        and must be 256-byte aligned
  * Supported: d in {64, 128}; h_q % h_kv == 0; q_len in [1, 16].
  */
 int attn_decode_gqa(const attn_paged_kv_t* kv, const void* q, void* out, float* lse,
@@ -297,6 +312,9 @@ int attn_decode_merge(const attn_plan_t* plan, int h_q, int d_v, attn_dtype_t dt
  *             latent caches hold rotated keys ("Hardware-Efficient Attention
  *             for Fast Decoding", review page, Core claim), GTA caches raw
  *             ones (pass rope_theta <= 0; the decode rotates them).
+ * A row whose position falls past the sequence's page-table row
+ * (pos / page_size >= max_pages_per_seq) or whose page-table entry is not in
+ * [0, num_pages) is skipped: nothing is written for it.
  * Copies are exact; rotated keys are rounded to kv->dtype.  Row starts and
  * row widths must be multiples of 16 bytes, d_rope even and at most 64.
  * Returns ATTN_OK once enqueued on `stream`, INVALID_ARG (nothing enqueued)
@@ -351,6 +369,33 @@ int attn_latent_project_output(const void* o_lat, const void* w_uv, void* out, i
  * every length fits the page table.  Returns ATTN_OK or INVALID_ARG.
  */
 int attn_paged_kv_check(const attn_paged_kv_t* host_copy);
+
+/*
+ * Measurement probes (not part of the decode path): the ceilings the decode
+ * kernels are compared with on the GPU they run on.  Decode is bound by
+ * reading the KV cache from HBM ("Hardware-Efficient Attention for Fast
+ * Decoding", review page, Core claim) or, at high arithmetic intensity, by
+ * the matrix cores (its Figure 3 caption, the roofline).
+ *
+ * attn_probe_stream_read: read `bytes` of device memory at `buf` once,
+ *   split into 64 KB blocks over a few workgroups per CU, with the
+ *   nontemporal hint; mode 0 loads into registers, mode 1 loads straight
+ *   into LDS (global_load_lds_dwordx4, the decode kernels' path).  The
+ *   bytes read are exactly `bytes`: time the launch with events on
+ *   `stream` to get the streaming-read rate.  `sink` is a device uint32
+ *   the kernel may write (to keep the loads); nothing else is written.
+ *   Requirements: `bytes` a positive multiple of 65536, `buf` 1024-byte
+ *   aligned; INVALID_ARG otherwise.
+ * attn_probe_mfma: every wave of two 4-wave workgroups per CU runs `iters`
+ *   rounds of 8 independent v_mfma_f32_16x16x32_bf16 products on register
+ *   operands; *flops_out (host) receives the launch's FLOPs (2 per
+ *   multiply-add) so that FLOPs / duration is the matrix cores' bf16 rate.
+ *   `sink` is a device float the kernel may write.
+ * Both return ATTN_OK once enqueued on `stream`.
+ */
+int attn_probe_stream_read(const void* buf, size_t bytes, int mode, uint32_t* sink,
+                           hipStream_t stream);
+int attn_probe_mfma(int iters, float* sink, double* flops_out, hipStream_t stream);
 
 /* Static description of a status code. */
 const char* attn_status_string(int status);

@@ -241,7 +241,13 @@ def test_paged_kv_needs_one_layout_for_both_pools():
 def _fake_call(kind="gqa", **over):
     """A decode call with fake (never dereferenced) aligned device pointers:
     validation must reject it before any launch."""
-    st, plan, _, _ = _plan([100, 200], groups=over.pop("plan_groups", 8), chunk=64)
+    st, plan, items, info = _plan(over.pop("plan_seqlens", [100, 200]),
+                                  groups=over.pop("plan_groups", 8), chunk=64,
+                                  q_len=over.pop("plan_q_len", 1),
+                                  causal=over.pop("plan_causal", 0))
+    edit = over.pop("edit_host", None)
+    if edit is not None:  # tamper with the host arrays the call checks
+        edit(items, info)
     plan.items, plan.seqinfo = 0x10000, 0x20000
     for k, v in over.pop("plan_fields", {}).items():
         setattr(plan, k, v)
@@ -259,6 +265,7 @@ def _fake_call(kind="gqa", **over):
             setattr(kv, k, v)
         else:
             args[k] = v
+    _fake_call.keep = (items, info)  # the plan's host arrays outlive the call
     if kind == "gqa":
         return binding.attn_decode_gqa(kv, args["q"], args["out"], args["lse"], args["q_len"],
                                        args["h_q"], args["groups"], args["d"], 0.1, args["flags"], plan,
@@ -298,7 +305,7 @@ def test_validation_rejects_before_launch():
 
 
 def test_merge_validation():
-    st, plan, _, _ = _plan([5000, 100], chunk=64)
+    st, plan, items, info = _plan([5000, 100], chunk=64)
     plan.items, plan.seqinfo = 0x10000, 0x20000
     need = binding.attn_decode_workspace_size(plan, 32, 128)
     M = binding.attn_decode_merge
@@ -306,10 +313,50 @@ def test_merge_validation():
     assert M(plan, 32, 128, binding.ATTN_BF16, 0x800000, need - 1, 0x700000, None, None) == binding.ATTN_ERR_WORKSPACE
     assert M(plan, 32, 128, 7, 0x800000, need, 0x700000, None, None) == binding.ATTN_ERR_INVALID_ARG
     assert M(plan, 32, 128, binding.ATTN_BF16, 0x800000, need, 0, None, None) == binding.ATTN_ERR_INVALID_ARG
-    st, plan, _, _ = _plan([100, 100])
+    # a plan whose host arrays were altered after planning is refused
+    info[1, 1] = 10_000                  # partial slots past the plan's count
+    assert M(plan, 32, 128, binding.ATTN_BF16, 0x800000, need, 0x700000, None, None) == binding.ATTN_ERR_INVALID_ARG
+    st, plan, items, info = _plan([100, 100])
     plan.items, plan.seqinfo = 0x10000, 0x20000
     # nothing split: a no-op that succeeds without touching the GPU
     assert M(plan, 32, 128, binding.ATTN_BF16, 0, 0, 0x700000, None, None) == binding.ATTN_OK
+    assert M(plan, 30, 128, binding.ATTN_BF16, 0, 0, 0x700000, None, None) == binding.ATTN_ERR_INVALID_ARG
+
+
+def _set(arr, idx, val):
+    def f(items, info):
+        (items if arr == "items" else info)[idx] = val
+    return f
+
+
+@pytest.mark.parametrize("kind", ["gqa", "gta", "latent"])
+def test_decode_checks_the_plan_against_the_descriptor(kind):
+    """The decode kernels take lengths, splits and chunks from the plan, not
+    from kv->seqlens: a plan whose lengths overrun the page table's row
+    (max_pages_per_seq * page_size = 256 here), a causal plan shorter than
+    q_len, or host arrays altered after planning are refused before any
+    launch (fake, never dereferenced device pointers)."""
+    E, WS = binding.ATTN_ERR_INVALID_ARG, binding.ATTN_ERR_WORKSPACE
+    d = dict(gqa=128, gta=128, latent=256)[kind]
+    ex = dict(d=d, ws_bytes=0)  # the plan is checked before the (missing) workspace
+    if kind == "latent":
+        ex.update(plan_groups=2, groups=2)
+    assert _fake_call(kind, **ex) == WS
+    assert _fake_call(kind, plan_seqlens=[256, 1], **ex) == WS            # exactly 4 pages of 64
+    assert _fake_call(kind, plan_seqlens=[100, 257], **ex) == E           # one token more
+    for edit in (_set("info", (1, 2), 300),        # length past the page-table row
+                 _set("info", (0, 0), 0),          # zero splits
+                 _set("info", (0, 3), 32),         # chunks no longer cover the length
+                 _set("info", (1, 1), 999),        # partial slots past the count
+                 _set("items", (0, 0), 2),         # a sequence that does not exist
+                 _set("items", (0, 1), 1),         # groups out of plan order
+                 _set("items", (1, 2), 7),         # a split past the sequence's count
+                 _set("items", (1, 3), 5)):        # first token off its chunk
+        assert _fake_call(kind, edit_host=edit, **ex) == E
+    # causal q_len 4: every length must hold at least the 4 query tokens
+    causal = dict(plan_q_len=4, plan_causal=1, q_len=4, flags=1, **ex)
+    assert _fake_call(kind, **causal) == WS
+    assert _fake_call(kind, edit_host=_set("info", (0, 2), 3), **causal) == E
 
 
 def _append_kv():

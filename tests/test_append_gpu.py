@@ -121,3 +121,47 @@ def test_decode_after_append(name, page_size):
     torch.cuda.synchronize()
     ref, ref_lse = oracle.decode(w, inp)
     H.compare(H.to_np(out), H.to_np(lse), ref, ref_lse, H.value_max(w, inp), f"{name}/append")
+
+
+@pytest.mark.parametrize("name", ["gqa", "mla"])
+def test_append_skips_rows_outside_the_table(name):
+    """Rows the append cannot place are skipped, leaving the pools
+    untouched: a position past the sequence's page-table row, a page-table
+    entry of -1, and a page id past the pools.  The one well-formed
+    sequence is written as the oracle writes it."""
+    T = 2
+    w = CASES[name].with_(batch=4, q_len=T, seqlen_lo=100, seqlen_hi=200, max_seqlen=256,
+                          page_size=16)
+    print(f"[append-bounds] {name}", flush=True)
+    inp = synth.make_inputs(w)
+    new0, new1, newr = _new_rows(w, T, seed=7)
+    theta = 10000.0 if w.kind == "latent" else 0.0
+    n_pages = inp["pool0"].shape[0]
+    max_pages = inp["page_table"].shape[1]
+    table = inp["page_table"].copy()
+    seqlens = inp["seqlens"].copy()
+    seqlens[1] = max_pages * w.page_size + T + 1       # past the table row
+    for b, bad in ((2, -1), (3, n_pages + 5)):          # unassigned / past the pools
+        L = int(seqlens[b])
+        for t in range(T):
+            table[b, (L - T + t) // w.page_size] = bad
+    d = H.to_device(w, inp)
+    d["page_table"] = torch.from_numpy(table).cuda()
+    d["seqlens"] = torch.from_numpy(seqlens).cuda()
+    dt = d["pool0"].dtype
+    binding.kv_append(d["pool0"], d["pool1"], d["rope"], d["page_table"], d["seqlens"],
+                      _dev(new0, dt), _dev(new1, dt), _dev(newr, dt), rope_theta=theta)
+    torch.cuda.synchronize()
+    # expected: only sequence 0's rows written
+    want = oracle.kv_append(inp["pool0"], inp["pool1"], inp["rope"], table[:1], seqlens[:1],
+                            w.page_size, new0[:1], None if new1 is None else new1[:1],
+                            None if newr is None else newr[:1], theta, w.dtype)
+    for k, (got_t, exp) in enumerate(zip((d["pool0"], d["pool1"], d["rope"]), want)):
+        if exp is None:
+            continue
+        got = got_t.float().cpu().numpy()
+        if k < 2 or theta <= 0:
+            assert np.array_equal(got, exp.astype(np.float32)), f"{name} pool{k}"
+        else:
+            diff = np.abs(got - exp)
+            assert (diff <= 2 ** -7 * np.abs(exp) + 2 ** -14).all(), f"{name} rope"

@@ -374,32 +374,92 @@ def test_gather_probe_streaming_kernels(kind, page_size):
 
 # ------------------------------------------------------------ full size
 FULL = ["gqa_fp32_tiny", "gqa_llama8b", "gta_8k", "mla", "gla2", "gla2_spec4_128k",
-        "gqa_llama8b_8k", "gqa4_8k", "mla_spec4_128k", "gqa_llama8b@P1", "gla2@P1"]
+        "gqa_llama8b_8k", "gqa4_8k", "mla_spec4_128k", "gqa_llama8b@P1", "gla2@P1",
+        "gta_8k@P1", "gqa4_8k@P1"]
+
+# (pool layout, plan delivery): token-major or head-major pools; the plan as
+# device arrays with the merge launched by the decode call, or the way the
+# benchmark runs it (in the launch arguments when it fits, the decode
+# deferring the merge to a separate attn_decode_merge launch)
+FULL_MODES = [("nhd", "device"), ("hnd", "device"), ("nhd", "bench"), ("hnd", "bench")]
+
+
+def _run_mode(w, d, layout, mode):
+    dd = _head_major(dict(d)) if layout == "hnd" else d
+    if mode == "device":
+        out, lse, plan = H.run(w, dd)
+        return out, lse, plan
+    sh = binding.shape(w.kind, binding.ATTN_BF16 if w.dtype == "bf16" else binding.ATTN_FP32,
+                       w.batch, w.q_len, w.h_q, w.groups, w.head_dim, w.d_rope, w.page_size,
+                       w.causal)
+    probe = binding.DevicePlan(sh, d["seqlens_host"], d["q"].device)
+    plan = binding.DevicePlan(sh, d["seqlens_host"], d["q"].device,
+                              inline=bool(probe.plan.inline_ok))
+    out, lse, plan, ws = binding.decode(
+        w.kind, dd["q"], dd["pool0"], dd["pool1"], dd["rope"], dd["page_table"], dd["seqlens"],
+        dd["seqlens_host"], groups=w.groups, scale=w.softmax_scale, causal=w.causal,
+        rope_theta=w.rope_theta, d_rope=w.d_rope, plan=plan, defer_merge=True)
+    binding.merge(plan, out, lse, ws)
+    return out, lse, plan
 
 
 @pytest.mark.slow
 @pytest.mark.parametrize("name", FULL)
 def test_full_size_sampled(name):
+    """Every benchmark workload at full size, in every pool layout and plan
+    delivery, including exactly the launch configuration the benchmark
+    times: properties on every row, and sampled sequences against the
+    oracle (computed once)."""
     base, _, pg = name.partition("@P")
     w = W[base] if not pg else W[base].with_(page_size=int(pg))
-    print(f"[full] {name}", flush=True)
     inp = synth.make_inputs(w)
     d = H.to_device(w, inp)
-    out, lse, plan = H.run(w, d)
-    torch.cuda.synchronize()
-    o = H.to_np(out)
-    l = H.to_np(lse)
-    # properties on every row: finite, and each output is a convex
-    # combination of its values, so bounded by the largest |value|
-    assert np.isfinite(o).all() and np.isfinite(l).all()
-    assert np.abs(o).max() <= H.value_max(w, inp) * (1 + 2 ** -7)
-    # sampled sequences against the oracle (longest, shortest, one random)
     L = inp["seqlens"]
     pick = sorted({int(np.argmax(L)), int(np.argmin(L)), int(np.random.default_rng(0).integers(len(L)))})
     ref, ref_lse = oracle.decode(w, inp, batch_index=pick)
-    H.compare(o[pick], l[pick], ref, ref_lse, H.value_max(w, inp, pick), f"{name}/full")
-    del d, out, lse
+    vmax_all, vmax = H.value_max(w, inp), H.value_max(w, inp, pick)
+    first = None
+    for layout, mode in FULL_MODES:
+        print(f"[full] {name} {layout} {mode}", flush=True)
+        out, lse, plan = _run_mode(w, d, layout, mode)
+        torch.cuda.synchronize()
+        o, l = H.to_np(out), H.to_np(lse)
+        # properties on every row: finite, and each output is a convex
+        # combination of its values, so bounded by the largest |value|
+        assert np.isfinite(o).all() and np.isfinite(l).all()
+        assert np.abs(o).max() <= vmax_all * (1 + 2 ** -7)
+        H.compare(o[pick], l[pick], ref, ref_lse, vmax, f"{name}/{layout}/{mode}")
+        # the same plan and layout-independent arithmetic: one result
+        if first is None:
+            first = (out, lse)
+        else:
+            assert torch.equal(first[0], out) and torch.equal(first[1], lse), (layout, mode)
+        del out, lse, plan
+    del d
     torch.cuda.empty_cache()
+
+
+# head-major pools with whole pages of 64 tokens and more, in both plan
+# deliveries: the paired-GTA kernel (even groups of at most 8 rows) and the
+# latent kernel's whole-tile path, as the benchmark runs them
+HEAD_MAJOR = ["gta_8k", "gta_h6", "gta_g4", "gqa_llama8b", "gqa4_8k", "gla2", "gla2_spec4", "mla",
+              "mla_spec4", "gla2_h40_q3", "mla_h72_q2", "gla8_share"]
+
+
+@pytest.mark.parametrize("name", HEAD_MAJOR)
+@pytest.mark.parametrize("page_size", [64, 128])
+@pytest.mark.parametrize("inline", [False, True])
+def test_head_major_whole_pages(name, page_size, inline):
+    w = SMALL[name].with_(page_size=page_size)
+    print(f"[hnd] {name} P={page_size} inline={inline}", flush=True)
+    inp = synth.make_inputs(w, tail_fill=np.nan, extra_pages=3)
+    d = _head_major(H.to_device(w, inp))
+    ref, ref_lse = oracle.decode(w, inp)
+    for chunk in (0, 128):
+        out, lse, _ = H.run(w, d, chunk_tokens=chunk, inline_plan=inline)
+        torch.cuda.synchronize()
+        H.compare(H.to_np(out), H.to_np(lse), ref, ref_lse, H.value_max(w, inp),
+                  f"{name}/hnd/P{page_size}/inline{inline}/chunk{chunk}")
 
 
 @pytest.mark.parametrize("name", ["mla", "gla2"])
