@@ -95,6 +95,10 @@ def lib():
     L.attn_decode_gqa.argtypes = ([POINTER(PagedKV), c_void_p, c_void_p, c_void_p, c_int, c_int,
                                    c_int, c_int] + common_tail)
     L.attn_decode_gqa.restype = c_int
+    L.attn_decode_gqa_static.argtypes = [POINTER(PagedKV), c_void_p, c_void_p, c_void_p, c_int,
+                                         c_int, c_int, c_int, c_float, c_int, POINTER(Plan),
+                                         c_void_p]
+    L.attn_decode_gqa_static.restype = c_int
     L.attn_decode_gta.argtypes = ([POINTER(PagedKV), c_void_p, c_void_p, c_void_p, c_int, c_int,
                                    c_int, c_int, c_int, c_int, c_float] + common_tail)
     L.attn_decode_gta.restype = c_int
@@ -156,6 +160,15 @@ def attn_decode_gqa(kv, q, out, lse, q_len, h_q, h_kv, d, scale, flags, plan, ws
                     stream) -> int:
     return lib().attn_decode_gqa(ctypes.byref(kv), q, out, lse, q_len, h_q, h_kv, d, scale,
                                  flags, ctypes.byref(plan), ws, ws_bytes, stream)
+
+
+def attn_decode_gqa_static(kv, q, out, lse, q_len, h_q, h_kv, d, scale, flags, plan,
+                           stream) -> int:
+    return lib().attn_decode_gqa_static(ctypes.byref(kv), q, out, lse, q_len, h_q, h_kv, d, scale,
+                                        flags, ctypes.byref(plan), stream)
+
+
+ATTN_STATIC_SCRATCH_BYTES = 16 << 20
 
 
 def attn_decode_gta(kv, q, out, lse, q_len, h_q, h_kv, d, d_rope, n_rope_heads, rope_theta,

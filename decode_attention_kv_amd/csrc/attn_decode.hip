@@ -9,6 +9,9 @@
 // (Hydragen's decomposition on the "Efficient Inference" tag page).
 #include "attn_device.h"
 
+#include <atomic>
+#include <mutex>
+
 namespace attn_dev {
 namespace {
 
@@ -151,8 +154,7 @@ int check_plan(const attn_plan_t* plan, int64_t capacity, int min_len) {
 }
 
 int validate(const attn_paged_kv_t* kv, const void* q, const void* out, int q_len, int h_q,
-             int groups, int flags, const attn_plan_t* plan, const void* ws, size_t ws_bytes, int d_v,
-             bool need_pool1, bool need_rope) {
+             int groups, int flags, const attn_plan_t* plan, bool need_pool1, bool need_rope) {
   if (!kv || !q || !out || !plan) return ATTN_ERR_INVALID_ARG;
   if (!kv->pool0 || !kv->page_table || !kv->seqlens) return ATTN_ERR_INVALID_ARG;
   if (need_pool1 && !kv->pool1) return ATTN_ERR_INVALID_ARG;
@@ -180,12 +182,14 @@ int validate(const attn_paged_kv_t* kv, const void* q, const void* out, int q_le
       return ATTN_ERR_INVALID_ARG;
     if (kv->rope_token_stride < 0 || kv->rope_page_stride < 0) return ATTN_ERR_INVALID_ARG;
   }
-  const int pst = check_plan(plan, (int64_t)kv->max_pages_per_seq * kv->page_size,
-                             (flags & ATTN_CAUSAL) && q_len > 1 ? q_len : 0);
-  if (pst != ATTN_OK) return pst;
+  return check_plan(plan, (int64_t)kv->max_pages_per_seq * kv->page_size,
+                    (flags & ATTN_CAUSAL) && q_len > 1 ? q_len : 0);
+}
+
+// the caller's workspace: large enough for the plan and 256-byte aligned
+int check_workspace(const attn_plan_t* plan, int h_q, int d_v, const void* ws, size_t ws_bytes) {
   const size_t need = attn_decode_workspace_size(plan, h_q, d_v);
-  if (need > 0 && (!ws || ws_bytes < need || ((uintptr_t)ws & 255u)))
-    return ATTN_ERR_WORKSPACE;
+  if (need > 0 && (!ws || ws_bytes < need || ((uintptr_t)ws & 255u))) return ATTN_ERR_WORKSPACE;
   return ATTN_OK;
 }
 
@@ -286,19 +290,12 @@ void rope_table(Params& p, int d_rope, float theta) {
   p.rope_on = 1;
 }
 
-}  // namespace
-}  // namespace attn_dev
-
-using namespace attn_dev;
-
-extern "C" {
-
-int attn_decode_gqa(const attn_paged_kv_t* kv, const void* q, void* out, float* lse, int q_len,
-                    int h_q, int h_kv, int d, float softmax_scale, int flags,
-                    const attn_plan_t* plan, void* ws, size_t ws_bytes, hipStream_t stream) {
-  int st = validate(kv, q, out, q_len, h_q, h_kv, flags, plan, ws, ws_bytes, d, true, false);
-  if (st != ATTN_OK) return st;
-  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+// GQA decode after validation, with workspace `ws` (the caller's, or the
+// library's own device array for attn_decode_gqa_static).
+int decode_gqa(const attn_paged_kv_t* kv, const void* q, void* out, float* lse, int q_len,
+               int h_q, int h_kv, int d, float softmax_scale, int flags, const attn_plan_t* plan,
+               void* ws, hipStream_t stream) {
+  int st = ATTN_OK;
   Params p;
   fill_common(p, kv, q, out, lse, q_len, h_q, h_kv, softmax_scale, flags, plan, ws, d);
   const attn_internal::KernelChoice kc =
@@ -321,14 +318,86 @@ int attn_decode_gqa(const attn_paged_kv_t* kv, const void* q, void* out, float* 
   return d == 128 ? run<GQA, float, 128, 0>(p, plan, flags, stream) : run<GQA, float, 64, 0>(p, plan, flags, stream);
 }
 
+
+}  // namespace
+}  // namespace attn_dev
+
+// Workspace of attn_decode_gqa_static: one array per GPU, in the library's
+// code object, held until the process ends.  Host code never passes this name
+// to a kernel or a copy (on the host it stands for a host-side shadow, not a
+// device address); it uses the per-device address that static_scratch()
+// looks up instead.
+static __device__ __align__(256) char scratch[ATTN_STATIC_SCRATCH_BYTES];
+
+namespace attn_dev {
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+std::atomic<void*> scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+int static_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ATTN_ERR_HIP;
+  void* ptr = scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!ptr) {
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    ptr = scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!ptr) {
+      if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr)
+        return ATTN_ERR_HIP;
+      scratch_ptr[dev].store(ptr, std::memory_order_release);
+    }
+  }
+  *out = ptr;
+  return ATTN_OK;
+}
+
+}  // namespace
+}  // namespace attn_dev
+
+using namespace attn_dev;
+
+extern "C" {
+
+int attn_decode_gqa(const attn_paged_kv_t* kv, const void* q, void* out, float* lse, int q_len,
+                    int h_q, int h_kv, int d, float softmax_scale, int flags,
+                    const attn_plan_t* plan, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = validate(kv, q, out, q_len, h_q, h_kv, flags, plan, true, false);
+  if (st != ATTN_OK) return st;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  st = check_workspace(plan, h_q, d, ws, ws_bytes);
+  if (st != ATTN_OK) return st;
+  return decode_gqa(kv, q, out, lse, q_len, h_q, h_kv, d, softmax_scale, flags, plan, ws, stream);
+}
+
+int attn_decode_gqa_static(const attn_paged_kv_t* kv, const void* q, void* out, float* lse,
+                           int q_len, int h_q, int h_kv, int d, float softmax_scale, int flags,
+                           const attn_plan_t* plan, hipStream_t stream) {
+  int st = validate(kv, q, out, q_len, h_q, h_kv, flags, plan, true, false);
+  if (st != ATTN_OK) return st;
+  if (flags & ATTN_DEFER_MERGE) return ATTN_ERR_INVALID_ARG;  // partials unreachable
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (attn_decode_workspace_size(plan, h_q, d) > ATTN_STATIC_SCRATCH_BYTES)
+    return ATTN_ERR_WORKSPACE;
+  void* ws = nullptr;
+  st = static_scratch(&ws);
+  if (st != ATTN_OK) return st;
+  return decode_gqa(kv, q, out, lse, q_len, h_q, h_kv, d, softmax_scale, flags, plan, ws, stream);
+}
+
 int attn_decode_gta(const attn_paged_kv_t* kv, const void* q, void* out, float* lse, int q_len,
                     int h_q, int h_kv, int d, int d_rope, int n_rope_heads, float rope_theta,
                     float softmax_scale, int flags, const attn_plan_t* plan, void* ws,
                     size_t ws_bytes, hipStream_t stream) {
-  int st = validate(kv, q, out, q_len, h_q, h_kv, flags, plan, ws, ws_bytes, d, false, true);
+  int st = validate(kv, q, out, q_len, h_q, h_kv, flags, plan, false, true);
   if (st != ATTN_OK) return st;
   if (n_rope_heads != 1 || d_rope <= 0 || d_rope >= d) return ATTN_ERR_INVALID_ARG;
   if (kv->dtype != ATTN_BF16 || d != 128 || d_rope != 64) return ATTN_ERR_UNSUPPORTED;
+  st = check_workspace(plan, h_q, d, ws, ws_bytes);
+  if (st != ATTN_OK) return st;
   Params p;
   fill_common(p, kv, q, out, lse, q_len, h_q, h_kv, softmax_scale, flags, plan, ws, d);
   if (rope_theta > 0.f) rope_table(p, d_rope, rope_theta);
@@ -348,10 +417,12 @@ int attn_decode_latent(const attn_paged_kv_t* kv, const void* q, void* out, floa
                        int q_len, int h_q, int h_c, int d_c, int d_rope, float softmax_scale,
                        int flags, const attn_plan_t* plan, void* ws, size_t ws_bytes,
                        hipStream_t stream) {
-  int st = validate(kv, q, out, q_len, h_q, h_c, flags, plan, ws, ws_bytes, d_c, false, true);
+  int st = validate(kv, q, out, q_len, h_q, h_c, flags, plan, false, true);
   if (st != ATTN_OK) return st;
   if (kv->dtype != ATTN_BF16 || d_rope != 64 || (d_c != 512 && d_c != 256))
     return ATTN_ERR_UNSUPPORTED;
+  st = check_workspace(plan, h_q, d_c, ws, ws_bytes);
+  if (st != ATTN_OK) return st;
   Params p;
   fill_common(p, kv, q, out, lse, q_len, h_q, h_c, softmax_scale, flags, plan, ws, d_c);
   const attn_internal::KernelChoice kc =

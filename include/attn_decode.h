@@ -255,6 +255,30 @@ int attn_decode_gqa(const attn_paged_kv_t* kv, const void* q, void* out, float* 
                     hipStream_t stream);
 
 /*
+ * Allocation-free GQA decode, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  The same call and results as attn_decode_gqa (the
+ * same kernels, bit for bit), without the workspace argument: the split
+ * partials live in a device array of ATTN_STATIC_SCRATCH_BYTES inside the
+ * library, one per GPU the library runs on, held until the process ends
+ * (its device address is looked up once per device, on the first call made
+ * with that device current).  No call allocates or frees memory, and
+ * nothing in the array needs to start at zero.
+ * Every call on one GPU shares that array and it keeps the last call's
+ * contents: calls that overlap in time on one GPU (several streams or host
+ * threads) race on it, so the caller must serialise them.
+ * Errors: as attn_decode_gqa; ATTN_ERR_WORKSPACE when the plan needs more
+ * than ATTN_STATIC_SCRATCH_BYTES (attn_decode_workspace_size(plan, h_q, d)
+ * > ATTN_STATIC_SCRATCH_BYTES); INVALID_ARG with ATTN_DEFER_MERGE (the
+ * partials would be out of the caller's reach); ATTN_ERR_HIP when the
+ * array's device address cannot be obtained.
+ */
+#define ATTN_STATIC_SCRATCH_BYTES (16u << 20)
+int attn_decode_gqa_static(const attn_paged_kv_t* kv, const void* q, void* out, float* lse,
+                           int q_len, int h_q, int h_kv, int d, float softmax_scale, int flags,
+                           const attn_plan_t* plan, hipStream_t stream);
+
+/*
  * GTA decode: tied state pool0 [.., h_kv, d], single-head RoPE key
  * rope_pool [.., n_rope_heads = 1, d_rope].  With rope_theta > 0 the key's
  * RoPE slice and the query's last d_rope entries are rotated in the kernel;
