@@ -50,6 +50,7 @@ struct Params {
   const int32_t* seqinfo;
   int32_t q_len, h_q, g, rows;  // rows = g * q_len per group
   int32_t n_items, row_blocks;
+  int32_t nrb;  // GQA/GTA streaming kernel: workgroups (blocks of 16 RT rows) per item
   int32_t causal;
   int32_t rope_on;  // GTA: rotate the key's and query's RoPE slices in-kernel
   float scale_log2;

@@ -71,6 +71,12 @@ inline bool env_gta_pair() {
   static const bool v = env_int("ATTN_GTA_PAIR", 1) != 0;
   return v;
 }
+// ATTN_NARROW_RT4=1: groups of 33-64 rows in one workgroup of four row
+// tiles per wave (one wave per SIMD) instead of two 32-row workgroups
+inline bool env_narrow_rt4() {
+  static const bool v = env_int("ATTN_NARROW_RT4", 0) != 0;
+  return v;
+}
 inline bool env_force_general() {
   static const bool v = env_int("ATTN_FORCE_GENERAL", 0) != 0;
   return v;
@@ -121,11 +127,14 @@ inline KernelChoice choose_kernel(const attn_shape_t& sh) {
     const int lds = k.stages * narrow_stage_bytes(sh.kind, sh.head_dim, sh.d_rope) + 2048;
     int w = 163840 / lds;
     k.wgs_per_cu = w < 1 ? 1 : w > 2 ? 2 : w;
-    // more than 32 rows (four row tiles per wave): one wave per SIMD, and on
-    // pages of 16 tokens or more a shallower ring, which frees registers for
-    // the row tiles (GTA: 2 stages, measured +6 % over 5 at q_len 8; GQA
-    // with 128-wide heads: 3, +1.5 % over 4; 64-wide heads keep 6)
-    if (k.rows > 32) {
+    // more than 32 rows: two workgroups of 32 rows on one XCD (the second
+    // reads the item's rows from its L2), each as a group of 32 rows
+    if (k.rows > 32 && !env_narrow_rt4()) k.row_blocks = (k.rows + 31) / 32;
+    // with ATTN_NARROW_RT4=1, four row tiles per wave: one wave per SIMD,
+    // and on pages of 16 tokens or more a shallower ring, which frees
+    // registers for the row tiles (GTA: 2 stages, measured +6 % over 5 at
+    // q_len 8; GQA with 128-wide heads: 3, +1.5 % over 4)
+    if (k.rows > 32 && env_narrow_rt4()) {
       k.wgs_per_cu = 1;
       if (sh.page_size >= 16 && env_stages() == 0) {
         if (sh.kind == ATTN_KIND_GTA) k.stages = 2;

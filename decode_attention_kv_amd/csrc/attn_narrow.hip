@@ -256,11 +256,15 @@ void decode_narrow(Params p) {
   // (GTA's RoPE key rows are read by every group); gsz = 1 keeps plan order.
   // With a work queue (GQA) the grid holds as many workgroups as the GPU
   // keeps resident: block i takes item i first, and later items go to the
-  // workgroups that finish first, whatever their XCD.
+  // workgroups that finish first, whatever their XCD.  Groups of more than
+  // 32 rows split into nrb workgroups of 32 rows (row block rblk), which
+  // run on the same XCD: the second reads the item's cache rows from its L2.
   const int gsz = p.row_blocks;  // items per unit kept on one XCD
+  const int nrb = p.nrb;         // workgroups per item
   const int bid = blockIdx.x;
-  const int blk = bid / (8 * gsz);
-  const int rem = bid - blk * 8 * gsz;
+  const int blk = bid / (8 * gsz * nrb);
+  const int rem = bid - blk * 8 * gsz * nrb;
+  const int rblk = (rem >> 3) % nrb;
   __shared__ int next_item;
   uint32_t ticket = 0;
 
@@ -284,7 +288,7 @@ void decode_narrow(Params p) {
   // GTA2 works on pairs of plan items: items 2i and 2i + 1 are groups
   // j, j + 1 (j even) of one (sequence, chunk)
   const int n_units = PAIR ? p.n_items / 2 : p.n_items;
-  for (int item = (blk * 8 + (rem & 7)) * gsz + (rem >> 3); item < n_units;) {
+  for (int item = (blk * 8 + (rem & 7)) * gsz + (rem >> 3) / nrb; item < n_units;) {
   const PlanItem pi = load_item(p, PAIR ? 2 * item : item);
   const int b = pi.b, j = pi.j, split = pi.split, t0 = pi.t0;
   const int n_splits = pi.n_splits, slot_base = pi.slot_base, L = pi.L, chunk = pi.chunk;
@@ -300,7 +304,7 @@ void decode_narrow(Params p) {
   bool row_ok[RT], row_b[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    const int row = rt * 16 + col;
+    const int row = rblk * 16 * RT + rt * 16 + col;
     row_ok[rt] = row < (PAIR ? 2 : 1) * p.rows;
     row_b[rt] = PAIR && row >= p.rows;
     const int rr = row_b[rt] ? row - p.rows : row;
@@ -764,8 +768,9 @@ void decode_narrow(Params p) {
   if (n_splits > 1 && p.fuse_merge) {
 #pragma unroll
     for (int jj = j; jj < j + (PAIR ? 2 : 1); ++jj)
-      arrive_and_merge<D>(p, p.counters + (int64_t)b * (p.h_q / p.g) + jj, &merge_last, b, jj, 0,
-                          p.rows, n_splits, slot_base);
+      arrive_and_merge<D>(p, p.counters + ((int64_t)b * (p.h_q / p.g) + jj) * nrb + rblk,
+                          &merge_last, b, jj, rblk * 16 * RT, min(16 * RT, p.rows - rblk * 16 * RT),
+                          n_splits, slot_base);
   }
 
   // next item from the queue.  Every processed item draws one ticket, so
@@ -800,9 +805,11 @@ int launch_narrow_s(Params p, int n_items, int groups, hipStream_t stream) {
     // GTA2: a unit is a pair of plan items (two groups)
     const int gsz = KIND == GTA ? groups : KIND == GTA2 ? groups / 2 : 1;
     const int units = KIND == GTA2 ? n_items / 2 : n_items;
+    const int nrb = (p.rows + 16 * RT - 1) / (16 * RT);  // workgroups per item
     p.row_blocks = gsz;
-    int blocks = (units + 8 * gsz - 1) / (8 * gsz) * 8 * gsz;
-    if (p.queue && KIND == GQA && p.queue_base > 0 && p.queue_base < n_items) {
+    p.nrb = nrb;
+    int blocks = (units + 8 * gsz - 1) / (8 * gsz) * 8 * gsz * nrb;
+    if (p.queue && KIND == GQA && nrb == 1 && p.queue_base > 0 && p.queue_base < n_items) {
       blocks = p.queue_base;  // resident workgroups; the rest come from the queue
     } else {
       p.queue = nullptr;
@@ -838,7 +845,10 @@ int launch_narrow(const Params& p, int n_items, int groups, int stages, hipStrea
   if constexpr (KIND == GTA2) return launch_narrow_rt<KIND, D, DR, 1>(p, n_items, groups, stages, stream);
   const int rt = (p.rows + 15) / 16;
   if (rt <= 1) return launch_narrow_rt<KIND, D, DR, 1>(p, n_items, groups, stages, stream);
-  if (rt <= 2) return launch_narrow_rt<KIND, D, DR, 2>(p, n_items, groups, stages, stream);
+  // more than 32 rows: two workgroups of two row tiles (two waves per SIMD),
+  // unless ATTN_NARROW_RT4=1 keeps them in one of four row tiles
+  if (rt <= 2 || !attn_internal::env_narrow_rt4())
+    return launch_narrow_rt<KIND, D, DR, 2>(p, n_items, groups, stages, stream);
   return launch_narrow_rt<KIND, D, DR, 4>(p, n_items, groups, stages, stream);
 }
 

@@ -64,10 +64,17 @@ __global__ __launch_bounds__(kProbeThreads) void probe_read_lds(const char* buf,
   if (r == 0x9e3779b9u) atomicXor(sink, r);
 }
 
-// Matrix-core throughput: every wave runs `iters` rounds of NACC independent
-// v_mfma_f32_16x16x32_bf16 products on register operands (no memory
-// traffic), then folds its accumulators into `sink`.
+// Matrix-core throughput: every wave runs `iters` rounds of kProbeAcc
+// independent v_mfma_f32_16x16x32_bf16 products on register operands (no
+// memory traffic), then folds its accumulators into `sink`.  The products
+// are written as asm with each accumulator tied to its own AGPRs: from the
+// builtin the compiler moved the accumulators between registers on every
+// round, which measured those moves instead of the matrix cores.  The same
+// accumulator is reused only kProbeAcc products later, past any dependency
+// window.
 constexpr int kProbeAcc = 8;
+#define PROBE_MFMA(c) \
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b))
 __global__ __launch_bounds__(kProbeThreads) void probe_mfma(int iters, float* sink) {
   bf16x8 a, b;
 #pragma unroll
@@ -75,19 +82,22 @@ __global__ __launch_bounds__(kProbeThreads) void probe_mfma(int iters, float* si
     a[i] = (__bf16)(1.0f + 0.0078125f * (float)((threadIdx.x + i) & 7));
     b[i] = (__bf16)(0.5f - 0.0078125f * (float)((threadIdx.x * 3 + i) & 7));
   }
-  f32x4 acc[kProbeAcc];
-#pragma unroll
-  for (int k = 0; k < kProbeAcc; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = c0, c2 = c0, c3 = c0, c4 = c0, c5 = c0, c6 = c0, c7 = c0;
   for (int it = 0; it < iters; ++it) {
-#pragma unroll
-    for (int k = 0; k < kProbeAcc; ++k)
-      acc[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[k], 0, 0, 0);
+    PROBE_MFMA(c0);
+    PROBE_MFMA(c1);
+    PROBE_MFMA(c2);
+    PROBE_MFMA(c3);
+    PROBE_MFMA(c4);
+    PROBE_MFMA(c5);
+    PROBE_MFMA(c6);
+    PROBE_MFMA(c7);
   }
-  float s = 0.f;
-#pragma unroll
-  for (int k = 0; k < kProbeAcc; ++k) s += acc[k][0] + acc[k][1] + acc[k][2] + acc[k][3];
+  const f32x4 t = c0 + c1 + c2 + c3 + c4 + c5 + c6 + c7;
+  const float s = t[0] + t[1] + t[2] + t[3];
   if (s == 1234.5f) atomicAdd(sink, s);  // keeps the products; practically never taken
 }
+#undef PROBE_MFMA
 
 int cu_count() {
   int dev = 0, n = 0;
