@@ -143,12 +143,12 @@ inline KernelChoice choose_kernel(const attn_shape_t& sh) {
     }
     // GTA groups read the same RoPE key rows: keep them on one XCD's L2
     k.same_xcd_groups = sh.kind == ATTN_KIND_GTA;
-    // GTA with an even number of groups of at most 8 rows on pages of at
-    // least 64 tokens: one workgroup streams two groups, loading and
-    // rotating their common RoPE key rows once (40 KB stages, a ring of 3,
-    // one workgroup per CU; measured +4-5 % at page 64, -1.4 % at page 16)
-    if (sh.kind == ATTN_KIND_GTA && sh.groups % 2 == 0 && k.rows <= 8 && sh.page_size >= 64 &&
-        env_gta_pair()) {
+    // GTA with an even number of groups of at most 8 rows: one workgroup
+    // streams two groups, loading and rotating their common RoPE key rows
+    // once (40 KB stages, a ring of 3, one workgroup per CU; measured on GTA
+    // 8K against one group per workgroup: +11 % at page 1, +2.5-6 % at
+    // pages 2-64)
+    if (sh.kind == ATTN_KIND_GTA && sh.groups % 2 == 0 && k.rows <= 8 && env_gta_pair()) {
       k.pair = 2;
       k.stages = 3;
       k.wgs_per_cu = 1;

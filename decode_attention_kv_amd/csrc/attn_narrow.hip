@@ -222,7 +222,6 @@ void decode_narrow(Params p) {
   using G = Geo<KIND, D, DR>;
   constexpr bool TIED = KIND != GQA;   // tied state + one RoPE key head
   constexpr bool PAIR = KIND == GTA2;  // two groups per work item
-  static_assert(!(PAIR && SP), "paired groups need pages of at least 16 tokens");
   constexpr int DN = D - DR;          // key entries from the K / tied row
   constexpr int NKC = D / 32;         // 32-dim k-chunks of the score MFMA
   constexpr int NDVT = D / 16;        // 16-wide output tiles
@@ -351,6 +350,8 @@ void decode_narrow(Params p) {
       dma0.offsets_sp(o, ids, kw, t_last, pmask, p.page_stride, p.token_stride,
                       (int64_t)j * p.head_stride);
       dma0.issue_sp(dst + G::K_OFF, p.pool0, o);
+      // GTA2: the second group's rows sit one head further on
+      if constexpr (PAIR) dma0.issue_sp(dst + G::K2_OFF, p.pool0 + p.head_stride * 2, o);
       if constexpr (KIND == GQA) {
         dma0.issue_sp(dst + G::V_OFF, p.pool1, o);
       } else {
@@ -418,6 +419,16 @@ void decode_narrow(Params p) {
       }
     }
   }
+
+  // The cache loads are asm the compiler cannot count, and its s_waitcnt
+  // builtin orders no memory access, so a query load scheduled past the
+  // waits below would be taken as pending at the loop head and drained
+  // (vmcnt(0)) before every slice's first MFMA.  Redefining the query
+  // registers here makes the compiler wait for them once, before the loop.
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int c = 0; c < NKC; ++c) asm volatile("" : "+v"(qreg[rt][c]));
 
   f32x4 acc[RT][NDVT];
   float m_run[RT], l_run[RT];
@@ -822,13 +833,11 @@ int launch_narrow_s(Params p, int n_items, int groups, hipStream_t stream) {
 
 template <int KIND, int D, int DR, int RT>
 int launch_narrow_rt(const Params& p, int n_items, int groups, int stages, hipStream_t stream) {
-  // pages of fewer than 16 tokens: per-row page ids, rings of 2 or 4 stages
-  // (GTA2 is only chosen for pages of at least 64 tokens)
-  if constexpr (KIND != GTA2) {
-    if (p.page_shift < 4) {
-      return stages >= 4 ? launch_narrow_s<KIND, D, DR, RT, 4, true>(p, n_items, groups, stream)
+  // pages of fewer than 16 tokens: per-row page ids, rings of 2 to 4 stages
+  if (p.page_shift < 4 || attn_internal::env_int("ATTN_FORCE_SP", 0)) {
+    return stages >= 4   ? launch_narrow_s<KIND, D, DR, RT, 4, true>(p, n_items, groups, stream)
+           : stages == 3 ? launch_narrow_s<KIND, D, DR, RT, 3, true>(p, n_items, groups, stream)
                          : launch_narrow_s<KIND, D, DR, RT, 2, true>(p, n_items, groups, stream);
-    }
   }
   switch (stages) {
     case 2: return launch_narrow_s<KIND, D, DR, RT, 2>(p, n_items, groups, stream);
