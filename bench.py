@@ -88,19 +88,29 @@ def kernel_family(w):
 
 
 def kernel_sha(w):
-    """Hash of the sources of the workload's decode kernel: counter-based
-    traffic is reported only while it was taken on exactly these sources."""
+    """Hash of the sources of the workload's decode kernel and of the build
+    script (its compiler flags): counter-based traffic is reported only while
+    it was taken on exactly this code."""
     h = hashlib.sha256()
     for name in KERNEL_SRCS[kernel_family(w)]:
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(f.read())
+    with open(os.path.join(ROOT, "decode_attention_kv_amd", "_build.py"), "rb") as f:
+        h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def profile_tag(workload):
+    """File-name form of a workload name (overrides such as
+    gqa_llama8b_8k[page_size=1] become gqa_llama8b_8k_page_size_1)."""
+    import re
+    return re.sub(r"[^A-Za-z0-9_.-]+", "_", workload).strip("_")
 
 
 def load_traffic(workload, sha):
     """HBM bytes per decode launch from committed rocprofv3 counter runs,
     only if they were taken on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", f"decode_kernel_{workload}_counters.txt")
+    path = os.path.join(ROOT, "profiles", f"decode_kernel_{profile_tag(workload)}_counters.txt")
     if not os.path.exists(path):
         return None
     vals = {}
