@@ -26,6 +26,16 @@ constexpr int wide_kq(int d_c) { return d_c >= 512 ? WIDE_KQ512 : WIDE_KQ256; }
 constexpr int wide_rt(int d_c, int rows) {
   return (rows <= 32 || (d_c >= 512 && WIDE_KQ512 > 2)) ? 1 : 2;
 }
+inline int env_int(const char* name, int dflt);
+// 256-wide latents on pages of at least 64 tokens with more than 64 rows
+// per group (multi-token and speculative decode): four row tiles per wave
+// and a two-way key split, 128 rows per workgroup of four waves (one per
+// SIMD), which halves the LDS operand bytes per row against two row tiles;
+// ATTN_WIDE_RT4=0 keeps 64-row workgroups
+inline bool wide_rows128(int d_c, int rows, int page_size) {
+  static const bool on = env_int("ATTN_WIDE_RT4", 1) != 0;
+  return on && d_c == 256 && rows > 64 && page_size >= 64;
+}
 constexpr int kNarrowWaves = 4;    // waves per workgroup of the streaming kernel
 constexpr int kNarrowStageTarget = 65536;  // LDS bytes of the streaming ring
 
@@ -112,7 +122,8 @@ inline KernelChoice choose_kernel(const attn_shape_t& sh) {
   if (k.narrow && sh.kind == ATTN_KIND_LATENT) {
     k.stages = sh.head_dim >= 512 ? 2 : 3;
     k.wgs_per_cu = 1;
-    const int wg_rows = 32 * wide_rt(sh.head_dim, k.rows);
+    const int wg_rows =
+        wide_rows128(sh.head_dim, k.rows, sh.page_size) ? 128 : 32 * wide_rt(sh.head_dim, k.rows);
     k.row_blocks = (k.rows + wg_rows - 1) / wg_rows;
     k.same_xcd_groups = true;  // groups share RoPE rows, row blocks latent rows
     // a latent workgroup streams at its own pace: timelines show the same

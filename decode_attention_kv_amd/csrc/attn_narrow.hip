@@ -599,7 +599,9 @@ void decode_narrow(Params p) {
     // The running max is only raised (and O, l rescaled) when a row's max
     // grows by more than 2^8: probabilities then stay below 256, harmless in
     // fp32 and bf16, and most slices skip the rescale of the accumulators.
-    const bool full = (key0 + KW <= t_end) && !p.causal;
+    // keys below L - q_len + 1 are visible to every row of a causal group,
+    // so only the slices that reach past that (or past the chunk) mask
+    const bool full = key0 + KW <= (p.causal ? min(t_end, L - p.q_len + 1) : t_end);
     float s[RT][4];
     bool any_raise = false;
     float m_upd[RT];

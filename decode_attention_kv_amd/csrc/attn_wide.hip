@@ -2,10 +2,14 @@
 //
 // A latent group's keys are [latent_j || RoPE] rows and its values are the
 // latent rows themselves ("Hardware-Efficient Attention for Fast Decoding",
-// Core claim; the MLA and GLA definitions).  One workgroup of four waves
+// Core claim; the MLA and GLA definitions).  One workgroup of 2 KQ waves
 // holds 32*RT query rows of a group (the group's heads times the query
 // tokens, or a block of them) and streams the rows of its chunk through a
 // ring of STAGES 64-key LDS stages filled by direct global->LDS loads.
+// Configurations (RT, KQ): 256-wide latents (2, 4), eight waves two per
+// SIMD, or (4, 2) for groups of more than 64 rows, four waves of 64 rows
+// each, which halves the LDS operand bytes per row (the bound of this
+// kernel at high intensity); 512-wide latents (2, 2).
 //
 // Work split inside a workgroup of 2 KQ waves: wave (kq, rh) owns the row
 // half rh (16*RT rows) and
@@ -17,6 +21,13 @@
 // So every K element is read from LDS by two waves (one per row half) and
 // every V element by two (one per row half), half of what a split over rows
 // alone needs.
+//
+// Tile schedules.  Plain: per tile, wait for its stage, scores, softmax,
+// exchange barrier, P V.  Pipelined (256-wide latents, groups of more than
+// 64 rows): step i computes the scores of tile i, then P V of tile i - 1
+// with tile i's softmax interleaved into those MFMAs, behind one barrier
+// per step; probabilities alternate between two LDS buffers and one tile
+// is in flight instead of two.
 //
 // LDS layout of a stage (64 banks of 4 bytes, 16 lanes served per cycle):
 // the 16-byte K reads of 16 consecutive keys and the transposing V^T reads
@@ -32,10 +43,12 @@
 // Softmax: every row keeps a fixed reference max m_ref, the pair-wide max
 // of its first tile (the visible keys of a chunk are a prefix of it, so
 // rows with any visible key have one there), and O is never rescaled;
-// probabilities exp2(s - m_ref) are exact until a score exceeds m_ref by
-// 2^64 (log2 units).  A workgroup that sees such a score writes nothing and
-// sets its flag; a second launch redoes exactly those workgroups with the
-// classic online rescaling (RESCALE = true).
+// probabilities exp2(s - m_ref) stay far from fp32 and bf16 overflow while
+// every score is within 64 (log2 units) of m_ref.  A workgroup in which
+// some lane's running sum of probabilities passes 2^64 (as it does once a
+// score exceeds m_ref by 64) writes nothing and sets its flag; a second
+// launch redoes exactly those workgroups with the classic online rescaling
+// (RESCALE = true).
 //
 // Pages of at least 64 tokens hold whole tiles: one page id per tile, from
 // an LDS table filled once per item.  Smaller pages (SP = true, any power of
@@ -98,9 +111,15 @@ struct Item {
 
 constexpr int PT_MAX = 512;  // tiles whose page ids are kept in LDS
 
+// LDS of a workgroup: the ring, one probability buffer (two for the
+// pipelined schedule) and the page-id table
+template <int DC, int RT, int STAGES, bool PIPE> constexpr int wide_lds_bytes() {
+  return STAGES * Geo<DC, 64>::STAGE + (PIPE ? 2 : 1) * 4 * RT * 1024 + PT_MAX * 4;
+}
+
 // Stream the item's chunk and write its output rows; returns true, writing
 // nothing, when (RESCALE = false) some row outgrew its fixed reference.
-template <int DC, int DR, int RT, int STAGES, int KQ, bool RESCALE, bool SP>
+template <int DC, int DR, int RT, int STAGES, int KQ, bool RESCALE, bool SP, bool PIPE>
 __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* ring) {
   using G = Geo<DC, DR>;
   constexpr int NW = 2 * KQ;           // waves: key part kq = wave % KQ, row half wave / KQ
@@ -112,7 +131,7 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
   constexpr int LPW = G::LOADS / NW;   // loads per wave per stage
   constexpr int R_WG = 32 * RT;        // rows per workgroup
   constexpr int PBUF = STAGES * G::STAGE;
-  constexpr int PTAB = PBUF + 4 * RT * 1024;   // page-id table
+  constexpr int PTAB = PBUF + (PIPE ? 2 : 1) * 4 * RT * 1024;   // page-id table
   // small pages: wave w loads the rows of keys [KR w, KR w + KR) of a tile;
   // their page ids sit in a ring of STAGES slots of NW x 64 bytes at PTAB
   constexpr int KR = 64 / NW;
@@ -209,11 +228,9 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
     uint32_t sbase;
     int valid;  // rows of the tile that exist
   };
-  auto prepare = [&](int t, int u) __attribute__((always_inline)) {
+  auto prepare_page = [&](int t, int u, int64_t page) __attribute__((always_inline)) {
     const int tt = min(t, n_tiles - 1);
     const int key0 = t0 + tt * 64;                  // 64-aligned, inside one page
-    const int64_t page = tt < PT_MAX ? __builtin_amdgcn_readfirstlane(ptab[tt])
-                                     : sload_i32(pt_row + (key0 >> p.page_shift));
     const int slot0 = key0 & pmask;
     Fetch f;
     f.valid = min(64, t_end - key0);
@@ -223,6 +240,12 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
         uniform_ptr(p.rope + (page * p.rpage_stride + (int64_t)slot0 * p.rtoken_stride) * 2);
     f.sbase = ring_base + u * G::STAGE;
     return f;
+  };
+  auto prepare = [&](int t, int u) __attribute__((always_inline)) {
+    const int tt = min(t, n_tiles - 1);
+    const int64_t page = tt < PT_MAX ? __builtin_amdgcn_readfirstlane(ptab[tt])
+                                     : sload_i32(pt_row + ((t0 + tt * 64) >> p.page_shift));
+    return prepare_page(t, u, page);
   };
   auto issue_load = [&](const Fetch& f, int k) __attribute__((always_inline)) {
     const int blk = wave + NW * (k < LK ? k : k - LK);
@@ -364,7 +387,6 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
   // per lane; a 32-key chunk's B operand is blocks 2 kc and 2 kc + 1
   char* const pbuf = ring + PBUF;
   const int p_lane = rh * 4 * RT * 512 + lane * 8;   // + (block * RT + rt) * 512
-  float* const tex = reinterpret_cast<float*>(pbuf);     // tile-max exchange (aliases pbuf)
   const int t_wr = ((rh * KQ + kq) * RT) * 16 + col;    // + rt * 16; partners kq'
   const int t_rh = (rh * KQ * RT) * 16 + col;           // + (kq' * RT + rt) * 16
 
@@ -377,100 +399,67 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
 #pragma unroll
     for (int i = 0; i < NDVW; ++i) acc[rt][i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  bool over = false;
 
   float neg_m[RT];  // -(reference max), fixed after the first tile
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) neg_m[rt] = 0.f;
 
-  if (n_tiles > 0) {
-#pragma unroll
-    for (int u = 0; u < STAGES - 1; ++u) issue(u, u);
-  }
-
-  // One tile in stage U; when U is a compile-time constant every LDS operand
-  // address is a per-lane base plus an immediate.
-  auto tile = [&](int t, auto ucst) __attribute__((always_inline)) {
-    const int U = static_cast<int>(ucst);
-    {
-      // loads per tile and wave: LPW cache loads (+ one page-id load)
-      constexpr int ahead = (STAGES - 2) * (LPW + (SP ? 1 : 0));
-      __builtin_amdgcn_s_waitcnt((ahead & 15) | ((ahead >> 4) << 14) | (0x7 << 4) | (0xf << 8));
-    }
-    // every wave's loads of tile t have landed, and every wave is done with
-    // tile t - 1 (its stage and the probability buffer are free again)
-    __syncthreads();
-    // refill the stage of tile t - 1 with tile t + STAGES - 1: a full tile's
-    // loads are spread over the score MFMAs below, a partial one's issued now
-    // (small pages: always spread, after the page ids of tile t + 2 STAGES - 2)
-    const auto nf = [&]() __attribute__((always_inline)) {
-      if constexpr (SP)
-        return prepare_sp(t + STAGES - 1, (U + STAGES - 1) % STAGES);
-      else
-        return prepare(t + STAGES - 1, (U + STAGES - 1) % STAGES);
-    }();
-    bool spread = true;
-    if constexpr (SP) {
-      issue_ids(t + 2 * STAGES - 2);
-    } else {
-      spread = nf.valid == 64;
-      if (!spread) issue_clamped(nf);
-    }
-    const char* sb = ring + U * G::STAGE;
-    const int key0 = t0 + t * 64;
-
-    // scores S^T for this wave's KPW keys: MT M tiles x RT row tiles.  The K
-    // operand reads run KD steps ahead of the MFMAs that consume them
-    // (scheduling fences keep that order)
-    f32x4 sa[RT][MT];
+  // ---- the phases of a tile
+  // scores S^T of this wave's KPW keys of the tile at stage base sb: MT M
+  // tiles x RT row tiles.  The K operand reads run KD steps ahead of the
+  // MFMAs that consume them (scheduling fences keep that order); when
+  // `spread`, load k of the fetch nf is issued after step 2 k + 1.
+  auto score_phase = [&](const char* sb, const auto& nf, bool spread,
+                         f32x4 (&sa)[RT][MT]) __attribute__((always_inline)) {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) sa[rt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    {
-      constexpr int NS = MT * G::NKC;  // step = (chunk c, M tile mt)
-      static_assert(NS >= 2 * LPW, "every load finds a step");
-      constexpr int KD = DC >= 512 && RT > 1 ? WIDE_KD512 : 6;
-      auto kread = [&](int st) __attribute__((always_inline)) {
-        const int c = st / MT, mt = st % MT;
-        const char* src;
-        if (c < G::NKL)
-          src = sb + (((c >> 1) & 1) ? s_lat_m : s_lat_p) +
-                mt * (G::PAIR ? 8 : 16) * G::BSTR + c * 64;
+    constexpr int NS = MT * G::NKC;  // step = (chunk c, M tile mt)
+    static_assert(NS >= 2 * LPW, "every load finds a step");
+    constexpr int KD = DC >= 512 && RT > 1 ? WIDE_KD512 : 6;
+    auto kread = [&](int st) __attribute__((always_inline)) {
+      const int c = st / MT, mt = st % MT;
+      const char* src;
+      if (c < G::NKL)
+        src = sb + (((c >> 1) & 1) ? s_lat_m : s_lat_p) + mt * (G::PAIR ? 8 : 16) * G::BSTR +
+              c * 64;
+      else
+        src = sb + (c == G::NKL ? s_rope0 : s_rope1) + mt * 16 * 128;
+      return *reinterpret_cast<const bf16x8*>(src);
+    };
+    bf16x8 kb[KD];
+#pragma unroll
+    for (int st = 0; st < KD; ++st) kb[st] = kread(st);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      const int c = st / MT, mt = st % MT;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+        sa[rt][mt] =
+            __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[st % KD], qreg[rt][c], sa[rt][mt], 0, 0, 0);
+      if (st + KD < NS) kb[st % KD] = kread(st + KD);
+      if ((st & 1) && (st >> 1) < LPW && spread) {
+        if constexpr (SP)
+          issue_load_sp(nf, st >> 1);
         else
-          src = sb + (c == G::NKL ? s_rope0 : s_rope1) + mt * 16 * 128;
-        return *reinterpret_cast<const bf16x8*>(src);
-      };
-      bf16x8 kb[KD];
-#pragma unroll
-      for (int st = 0; st < KD; ++st) kb[st] = kread(st);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int st = 0; st < NS; ++st) {
-        const int c = st / MT, mt = st % MT;
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-          sa[rt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[st % KD], qreg[rt][c], sa[rt][mt],
-                                                               0, 0, 0);
-        if (st + KD < NS) kb[st % KD] = kread(st + KD);
-        if ((st & 1) && (st >> 1) < LPW && spread) {
-          if constexpr (SP)
-            issue_load_sp(nf, st >> 1);
-          else
-            issue_load(nf, st >> 1);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+          issue_load(nf, st >> 1);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
+  };
 
-    // x = scale * score - m_ref (log2 units); lane holds keys
-    // key0 + KPW kq + 16 mt + 4 grp + i of row col.  Masked keys of a partial
-    // or causal tile: key - (key0 + KPW kq + 4 grp) = 16 mt + i must stay
-    // below the row's limit min(t_end, qlimit + 1) - (key0 + KPW kq + 4 grp).
-    const bool full = (key0 + 64 <= t_end) && !p.causal;
+  // x = scale * score + nm (log2 units); lane holds keys
+  // key0 + KPW kq + 16 mt + 4 grp + i of row col.  Masked keys of a partial
+  // or causal tile: key - (key0 + KPW kq + 4 grp) = 16 mt + i must stay
+  // below the row's limit min(t_end, qlimit + 1) - (key0 + KPW kq + 4 grp).
+  // Keys below L - q_len + 1 are visible to every row of a causal group, so
+  // only tiles that reach past that (or past the chunk) mask.
+  auto scale_mask = [&](int key0, const f32x4 (&sa)[RT][MT], bool first,
+                        float (&x)[RT][MT][4]) __attribute__((always_inline)) {
+    const bool full = key0 + 64 <= (p.causal ? min(t_end, L - p.q_len + 1) : t_end);
     const int kbase = key0 + KPW * kq + 4 * grp;
-    float x[RT][MT][4], tmax[RT];
-    const bool first = RESCALE || t == 0;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       const float nm = first ? 0.f : neg_m[rt];
@@ -484,134 +473,274 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
           x[rt][mt][i] = v;
         }
     }
+  };
 
-    // reference max shared by the waves (kq = 0 .. KQ-1) of a row half: taken
-    // on the first tile (every tile when rescaling)
-    if (first) {
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, x[rt][mt][i]);
-        tmax[rt] = wave_max4(mx);
-      }
-      if (grp == 0) {
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) tex[t_wr + rt * 16] = tmax[rt];
-      }
-      __syncthreads();
-      float other[RT];
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        other[rt] = -INFINITY;
-#pragma unroll
-        for (int k2 = 0; k2 < KQ; ++k2) other[rt] = fmaxf(other[rt], tex[t_rh + (k2 * RT + rt) * 16]);
-      }
-      __syncthreads();  // the exchange slots alias the probability buffer
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        const float pair_max = fmaxf(tmax[rt], other[rt]);
-        if constexpr (RESCALE) {
-          const float m_new = fmaxf(m_ref[rt], pair_max);
-          const float a = __builtin_amdgcn_exp2f(m_ref[rt] - ((m_new == -INFINITY) ? 0.f : m_new));
-          l_run[rt] *= a;
-#pragma unroll
-          for (int dt = 0; dt < NDVW; ++dt) acc[rt][dt] *= a;
-          m_ref[rt] = m_new;
-        } else {
-          m_ref[rt] = pair_max;
-        }
-        neg_m[rt] = (m_ref[rt] == -INFINITY) ? 0.f : -m_ref[rt];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) x[rt][mt][i] += neg_m[rt];
-      }
-    }
-
-    float xmax = -INFINITY;
+  // reference max shared by the waves (kq = 0 .. KQ-1) of a row half through
+  // the slots `tx` (taken on the first tile; on every tile when rescaling);
+  // `realias`: the slots alias the probability buffer about to be written
+  auto take_reference = [&](float (&x)[RT][MT][4], float* tx,
+                            bool realias) __attribute__((always_inline)) {
+    float tmax[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      float psum = 0.f;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, x[rt][mt][i]);
+      tmax[rt] = wave_max4(mx);
+    }
+    if (grp == 0) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) tx[t_wr + rt * 16] = tmax[rt];
+    }
+    __syncthreads();
+    float other[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      other[rt] = -INFINITY;
+#pragma unroll
+      for (int k2 = 0; k2 < KQ; ++k2) other[rt] = fmaxf(other[rt], tx[t_rh + (k2 * RT + rt) * 16]);
+    }
+    if (realias) __syncthreads();
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const float pair_max = fmaxf(tmax[rt], other[rt]);
+      if constexpr (RESCALE) {
+        const float m_new = fmaxf(m_ref[rt], pair_max);
+        const float a = __builtin_amdgcn_exp2f(m_ref[rt] - ((m_new == -INFINITY) ? 0.f : m_new));
+        l_run[rt] *= a;
+#pragma unroll
+        for (int dt = 0; dt < NDVW; ++dt) acc[rt][dt] *= a;
+        m_ref[rt] = m_new;
+      } else {
+        m_ref[rt] = pair_max;
+      }
+      neg_m[rt] = (m_ref[rt] == -INFINITY) ? 0.f : -m_ref[rt];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[rt][mt][i] += neg_m[rt];
+    }
+  };
+
+  // probabilities exp2(x) into the running sums and, as bf16, into this
+  // wave's slots of the probability buffer pb
+  auto write_probs = [&](const float (&x)[RT][MT][4], char* pb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        bf16x4 pb;
+        bf16x4 pv;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          xmax = fmaxf(xmax, x[rt][mt][i]);
           const float e = __builtin_amdgcn_exp2f(x[rt][mt][i]);
-          psum += e;
-          pb[i] = (__bf16)e;
+          l_run[rt] += e;
+          pv[i] = (__bf16)e;
         }
-        *reinterpret_cast<bf16x4*>(pbuf + p_lane + ((kq * MT + mt) * RT + rt) * 512) = pb;
-      }
-      l_run[rt] += psum;
-    }
-    // a score more than 2^64 above the reference (log2 units)
-    if constexpr (!RESCALE) over |= xmax > 64.f;
-    __syncthreads();  // both key halves' probabilities are in the buffer
-
-    // O^T += V^T P^T over all 64 keys for this wave's value half; for the
-    // 32-key chunk kc the A operand holds keys 32 kc + 4 grp + e (e < 4)
-    // and 32 kc + 16 + 4 grp + (e - 4), matching the B operand written by
-    // waves kq with keys in that chunk
-    {
-      bf16x8 pk[2][RT];
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-          const bf16x4 lo = *reinterpret_cast<const bf16x4*>(pbuf + p_lane + ((2 * kc) * RT + rt) * 512);
-          const bf16x4 hi =
-              *reinterpret_cast<const bf16x4*>(pbuf + p_lane + ((2 * kc + 1) * RT + rt) * 512);
-          pk[kc][rt] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        }
-      // step = (kc, dt); the two V^T reads of a step run VD steps ahead
-      constexpr int NP = 2 * NDVW;
-      constexpr int VD = DC >= 512 && RT > 1 ? WIDE_VD512 : 4;
-      auto vread = [&](int st) __attribute__((always_inline)) {
-        const int kc = st / NDVW, dt = st % NDVW;
-        constexpr int RS = G::PAIR ? 16 : 32;   // blocks per 32 keys
-        const char* s0 = sb + ((NDVW % 8 == 0 && ((dt >> 2) & 1)) ? v_tr_m : v_tr_p) +
-                         kc * RS * G::BSTR + dt * 32;
-        const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(s0));
-        const bf16x4 v1 =
-            __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(s0 + RS / 2 * G::BSTR));
-        return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-      };
-      bf16x8 vb[VD];
-#pragma unroll
-      for (int st = 0; st < VD; ++st) vb[st] = vread(st);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int st = 0; st < NP; ++st) {
-        const int kc = st / NDVW, dt = st % NDVW;
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-          acc[rt][dt] =
-              __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb[st % VD], pk[kc][rt], acc[rt][dt], 0, 0, 0);
-        if (st + VD < NP) vb[st % VD] = vread(st + VD);
-        __builtin_amdgcn_sched_barrier(0);
+        *reinterpret_cast<bf16x4*>(pb + p_lane + ((kq * MT + mt) * RT + rt) * 512) = pv;
       }
     }
   };
 
-  // the tile loop, unrolled by the ring depth (constant stage addresses)
-  // except for 512-wide latents with two row tiles per wave, whose register
-  // budget does not hold two copies of the loop body
-  constexpr bool UNROLL = !(DC >= 512 && RT > 1);
-  if constexpr (UNROLL) {
-    for (int t = 0; t < n_tiles; t += STAGES) {
-      tile(t, std::integral_constant<int, 0>{});
-      if (t + 1 < n_tiles) tile(t + 1, std::integral_constant<int, 1>{});
-      if constexpr (STAGES > 2) {
-        if (t + 2 < n_tiles) tile(t + 2, std::integral_constant<int, 2>{});
+  // O^T += V^T P^T over all 64 keys of the tile at stage base sb for this
+  // wave's value part, probabilities from buffer pb; for the 32-key chunk
+  // kc the A operand holds keys 32 kc + 4 grp + e (e < 4) and
+  // 32 kc + 16 + 4 grp + (e - 4), matching the B operand written by the
+  // waves kq with keys in that chunk
+  auto pv_phase = [&](const char* sb, const char* pb, auto hook) __attribute__((always_inline)) {
+    bf16x8 pk[2][RT];
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(pb + p_lane + ((2 * kc) * RT + rt) * 512);
+        const bf16x4 hi =
+            *reinterpret_cast<const bf16x4*>(pb + p_lane + ((2 * kc + 1) * RT + rt) * 512);
+        pk[kc][rt] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       }
+    // step = (kc, dt); the two V^T reads of a step run VD steps ahead
+    constexpr int NP = 2 * NDVW;
+    constexpr int VD = DC >= 512 && RT > 1 ? WIDE_VD512 : 4;
+    auto vread = [&](int st) __attribute__((always_inline)) {
+      const int kc = st / NDVW, dt = st % NDVW;
+      constexpr int RS = G::PAIR ? 16 : 32;   // blocks per 32 keys
+      const char* s0 = sb + ((NDVW % 8 == 0 && ((dt >> 2) & 1)) ? v_tr_m : v_tr_p) +
+                       kc * RS * G::BSTR + dt * 32;
+      const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(s0));
+      const bf16x4 v1 =
+          __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(s0 + RS / 2 * G::BSTR));
+      return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    bf16x8 vb[VD];
+#pragma unroll
+    for (int st = 0; st < VD; ++st) vb[st] = vread(st);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int st = 0; st < NP; ++st) {
+      const int kc = st / NDVW, dt = st % NDVW;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+        acc[rt][dt] =
+            __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb[st % VD], pk[kc][rt], acc[rt][dt], 0, 0, 0);
+      if (st + VD < NP) vb[st % VD] = vread(st + VD);
+      hook(st);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  const auto no_hook = [](int) __attribute__((always_inline)) {};
+
+  if constexpr (!PIPE) {
+    if (n_tiles > 0) {
+#pragma unroll
+      for (int u = 0; u < STAGES - 1; ++u) issue(u, u);
+    }
+
+    // One tile in stage U; when U is a compile-time constant every LDS
+    // operand address is a per-lane base plus an immediate.
+    auto tile = [&](int t, auto ucst) __attribute__((always_inline)) {
+      const int U = static_cast<int>(ucst);
+      {
+        // loads per tile and wave: LPW cache loads (+ one page-id load)
+        constexpr int ahead = (STAGES - 2) * (LPW + (SP ? 1 : 0));
+        __builtin_amdgcn_s_waitcnt((ahead & 15) | ((ahead >> 4) << 14) | (0x7 << 4) | (0xf << 8));
+      }
+      // every wave's loads of tile t have landed, and every wave is done
+      // with tile t - 1 (its stage and the probability buffer are free again)
+      __syncthreads();
+      // refill the stage of tile t - 1 with tile t + STAGES - 1: a full
+      // tile's loads are spread over the score MFMAs, a partial one's issued
+      // now (small pages: always spread, after the page ids of tile
+      // t + 2 STAGES - 2)
+      const auto nf = [&]() __attribute__((always_inline)) {
+        if constexpr (SP)
+          return prepare_sp(t + STAGES - 1, (U + STAGES - 1) % STAGES);
+        else
+          return prepare(t + STAGES - 1, (U + STAGES - 1) % STAGES);
+      }();
+      bool spread = true;
+      if constexpr (SP) {
+        issue_ids(t + 2 * STAGES - 2);
+      } else {
+        spread = nf.valid == 64;
+        if (!spread) issue_clamped(nf);
+      }
+      const char* sb = ring + U * G::STAGE;
+      f32x4 sa[RT][MT];
+      score_phase(sb, nf, spread, sa);
+      float x[RT][MT][4];
+      const bool first = RESCALE || t == 0;
+      scale_mask(t0 + t * 64, sa, first, x);
+      if (first) take_reference(x, reinterpret_cast<float*>(pbuf), true);
+      write_probs(x, pbuf);
+      __syncthreads();  // every key part's probabilities are in the buffer
+      pv_phase(sb, pbuf, no_hook);
+    };
+
+    // the tile loop, unrolled by the ring depth (constant stage addresses)
+    // except for 512-wide latents with two row tiles per wave, whose
+    // register budget does not hold two copies of the loop body
+    constexpr bool UNROLL = !(DC >= 512 && RT > 1);
+    if constexpr (UNROLL) {
+      for (int t = 0; t < n_tiles; t += STAGES) {
+        tile(t, std::integral_constant<int, 0>{});
+        if (t + 1 < n_tiles) tile(t + 1, std::integral_constant<int, 1>{});
+        if constexpr (STAGES > 2) {
+          if (t + 2 < n_tiles) tile(t + 2, std::integral_constant<int, 2>{});
+        }
+      }
+    } else {
+      for (int t = 0; t < n_tiles; ++t) tile(t, t % STAGES);
     }
   } else {
-    for (int t = 0; t < n_tiles; ++t) tile(t, t % STAGES);
+    // Pipelined schedule: step i computes the scores of tile i and P V of
+    // tile i - 1, so each tile needs one barrier (instead of one for its
+    // stage and one for the probability exchange), and one wave's softmax
+    // overlaps the other waves' MFMAs.  A tile then lives in its stage for
+    // two steps: stage i % 3 holds tile i (scores), stage (i - 1) % 3 tile
+    // i - 1 (P V) and stage (i + 1) % 3 receives tile i + 1, issued over the
+    // score MFMAs of step i.  Probabilities alternate between two buffers.
+    static_assert(DC == 256 && STAGES == 3 && !SP && !RESCALE, "pipelined schedule");
+    constexpr int PBS = 4 * RT * 1024;
+    // page id of tile t (clamped to the last tile) from the LDS table, read
+    // a step before use; tiles past the table read the page table at use
+    auto page_of = [&](int t) __attribute__((always_inline)) {
+      return ptab[min(min(t, n_tiles - 1), PT_MAX - 1)];
+    };
+    int pid = 0;
+    auto step = [&](int i, auto ucst) __attribute__((always_inline)) {
+      const int U = static_cast<int>(ucst);
+      // tile i has landed (no other loads are in flight), every wave is done
+      // with step i - 1: tile i - 2's stage and probability buffer i % 2 are
+      // free, tile i - 1's probabilities are complete
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      __syncthreads();
+      const bool more = i + 1 < n_tiles;
+      const int tn = min(i + 1, n_tiles - 1);
+      const int64_t page = tn < PT_MAX ? __builtin_amdgcn_readfirstlane(pid)
+                                       : sload_i32(pt_row + ((t0 + tn * 64) >> p.page_shift));
+      const Fetch nf = prepare_page(i + 1, (U + 1) % 3, page);
+      pid = page_of(i + 2);
+      const bool spread = more && nf.valid == 64;
+      if (more && !spread) issue_clamped(nf);
+      f32x4 sa[RT][MT];
+      score_phase(ring + U * G::STAGE, nf, spread, sa);
+      if (i == 0) {
+        float x[RT][MT][4];
+        scale_mask(t0, sa, true, x);
+        take_reference(x, reinterpret_cast<float*>(pbuf + PBS), false);
+        write_probs(x, pbuf);
+      } else {
+        // this tile's softmax rides along the P V MFMAs of the previous one:
+        // probability u (row tile, M tile, element) after P V step u
+        const int key0 = t0 + i * 64;
+        const bool full = key0 + 64 <= (p.causal ? min(t_end, L - p.q_len + 1) : t_end);
+        if (!full) {
+          float x[RT][MT][4];
+          scale_mask(key0, sa, false, x);
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (x[rt][mt][e] == -INFINITY) sa[rt][mt][e] = -INFINITY;
+        }
+        char* const pw = pbuf + (i & 1) * PBS;
+        bf16x4 pv[RT][MT];
+        constexpr int NU = RT * MT * 4;
+        static_assert(NU % (2 * NDVW) == 0 || (2 * NDVW) % NU == 0, "units per step");
+        auto hook = [&](int st) __attribute__((always_inline)) {
+          constexpr int NP = 2 * NDVW;
+          constexpr int PER = NU >= NP ? NU / NP : 1;
+          if (NU < NP && st >= NU) return;
+#pragma unroll
+          for (int q = 0; q < PER; ++q) {
+            const int u = st * PER + q;
+            const int rt = u / (MT * 4), mt = (u / 4) % MT, e = u % 4;
+            const float ex = __builtin_amdgcn_exp2f(fmaf(sa[rt][mt][e], p.scale_log2, neg_m[rt]));
+            l_run[rt] += ex;
+            pv[rt][mt][e] = (__bf16)ex;
+            if (e == 3)
+              *reinterpret_cast<bf16x4*>(pw + p_lane + ((kq * MT + mt) * RT + rt) * 512) = pv[rt][mt];
+          }
+        };
+        pv_phase(ring + ((U + 2) % 3) * G::STAGE, pbuf + ((i - 1) & 1) * PBS, hook);
+      }
+    };
+    if (n_tiles > 0) {
+      issue(0, 0);
+      pid = page_of(1);
+      step(0, std::integral_constant<int, 0>{});
+      for (int i = 1; i < n_tiles; i += 3) {
+        step(i, std::integral_constant<int, 1>{});
+        if (i + 1 < n_tiles) step(i + 1, std::integral_constant<int, 2>{});
+        if (i + 2 < n_tiles) step(i + 2, std::integral_constant<int, 0>{});
+      }
+      __syncthreads();  // the last tile's probabilities are complete
+      const int ul = (n_tiles - 1) % 3;
+      pv_phase(ring + ul * G::STAGE, pbuf + ((n_tiles - 1) & 1) * PBS, no_hook);
+    }
   }
   __builtin_amdgcn_s_waitcnt(0);  // drain the clamped trailing loads
   __syncthreads();                // the ring is free
@@ -619,7 +748,14 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
   // ---- workgroup-wide restart decision and the pair's row sums
   int* const flag = reinterpret_cast<int*>(ring);
   float* const lx = reinterpret_cast<float*>(ring + 256);
-  // the vote over all lanes of the wave, taken before a single lane stores it
+  // A probability above 2^64 (a score more than 64 above the reference,
+  // log2 units) leaves a lane's running sum above 2^64 (or inf / NaN); so
+  // does a sum that large of smaller ones, which the rescaling pass also
+  // handles exactly.  The vote covers all lanes of the wave, taken before a
+  // single lane stores it.
+  bool over = false;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) over |= !(l_run[rt] <= 0x1p64f);
   const bool wave_over = __builtin_amdgcn_ballot_w64(over) != 0;
   if (!RESCALE && lane == 0) flag[wave] = wave_over ? 1 : 0;
   float lsum[RT];
@@ -687,14 +823,16 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
 // RESCALE = false: the fixed-reference pass; records per workgroup whether
 // it had to give up (flags[block]).  RESCALE = true: the fix-up pass, a
 // second launch over the same grid that only works where the flag is set.
-template <int DC, int DR, int RT, int STAGES, int KQ, bool RESCALE, bool SP>
+// PIPE: the pipelined tile schedule (fixed-reference pass only).
+template <int DC, int DR, int RT, int STAGES, int KQ, bool RESCALE, bool SP, bool PIPE>
 __global__ __launch_bounds__(2 * KQ * 64) __attribute__((amdgpu_waves_per_eu(KQ / 2, KQ / 2)))
 void decode_wide(Params p) {
   using G = Geo<DC, DR>;
-  static_assert(STAGES * G::STAGE + 4 * RT * 1024 + PT_MAX * 4 <= 160 * 1024, "LDS");
+  constexpr int LDS = wide_lds_bytes<DC, RT, STAGES, PIPE>();
+  static_assert(LDS <= 160 * 1024, "LDS");
   static_assert((STAGES - 2) * (G::LOADS / (2 * KQ) + 1) <= 63, "vmcnt range");
   static_assert(STAGES == 2 || STAGES == 3, "tile loop unrolled for 2 or 3 stages");
-  __shared__ __attribute__((aligned(1024))) char ring[STAGES * G::STAGE + 4 * RT * 1024 + PT_MAX * 4];
+  __shared__ __attribute__((aligned(1024))) char ring[LDS];
 
   if constexpr (RESCALE) {
     if (p.flags[blockIdx.x] == 0) return;
@@ -728,7 +866,7 @@ void decode_wide(Params p) {
   itm.t_end = min(itm.t0 + chunk, itm.L);
   itm.n_tiles = (itm.t_end - itm.t0 + 63) / 64;
 
-  const bool gave_up = stream<DC, DR, RT, STAGES, KQ, RESCALE, SP>(p, itm, ring);
+  const bool gave_up = stream<DC, DR, RT, STAGES, KQ, RESCALE, SP, PIPE>(p, itm, ring);
   if constexpr (!RESCALE) {
     if (threadIdx.x == 0) p.flags[blockIdx.x] = gave_up ? 1 : 0;
   }
@@ -743,11 +881,26 @@ int launch_wide_one(Params p, int n_items, hipStream_t stream) {
   const int n_groups = p.h_q / p.g;
   const int units = (n_items + n_groups - 1) / n_groups;   // (sequence, chunk) pairs
   const dim3 grid((units + 7) / 8 * 8 * n_groups * p.row_blocks);
-  hipLaunchKernelGGL((wide::decode_wide<DC, DR, RT, S, KQ, false, SP>), grid, dim3(2 * KQ * 64), 0,
-                     stream, p);
+  // The pipelined schedule holds one tile in flight instead of two but
+  // needs one barrier per tile instead of two: faster where the workgroup
+  // is bound by its MFMA and LDS work and several row blocks share each
+  // tile through the L2 (groups of more than 64 rows: speculative and
+  // multi-token decode), slower for a single row block, which streams from
+  // HBM.
+  bool launched = false;
+  if constexpr (DC == 256 && RT >= 2 && S == 3 && !SP) {
+    if (RT == 4 || p.row_blocks > 1) {
+      hipLaunchKernelGGL((wide::decode_wide<DC, DR, RT, S, KQ, false, SP, true>), grid,
+                         dim3(2 * KQ * 64), 0, stream, p);
+      launched = true;
+    }
+  }
+  if (!launched)
+    hipLaunchKernelGGL((wide::decode_wide<DC, DR, RT, S, KQ, false, SP, false>), grid,
+                       dim3(2 * KQ * 64), 0, stream, p);
   // fix-up pass: exits at once unless the first pass flagged the workgroup
-  hipLaunchKernelGGL((wide::decode_wide<DC, DR, RT, S, KQ, true, SP>), grid, dim3(2 * KQ * 64), 0,
-                     stream, p);
+  hipLaunchKernelGGL((wide::decode_wide<DC, DR, RT, S, KQ, true, SP, false>), grid,
+                     dim3(2 * KQ * 64), 0, stream, p);
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
@@ -761,6 +914,10 @@ template <int DC, int DR, bool SP>
 int launch_wide_sp(const Params& p, int n_items, hipStream_t stream) {
   constexpr int S = (DC >= 512) ? 2 : 3;
   constexpr int KQ = attn_internal::wide_kq(DC);
+  if constexpr (DC == 256 && !SP) {
+    if (attn_internal::wide_rows128(DC, p.rows, 64))
+      return launch_wide_one<DC, DR, 4, S, 2, SP>(p, n_items, stream);
+  }
   if constexpr (attn_internal::wide_rt(DC, 64) == 1) {
     return launch_wide_one<DC, DR, 1, S, KQ, SP>(p, n_items, stream);
   } else {

@@ -462,7 +462,7 @@ def test_head_major_whole_pages(name, page_size, inline):
                   f"{name}/hnd/P{page_size}/inline{inline}/chunk{chunk}")
 
 
-@pytest.mark.parametrize("name", ["mla", "gla2"])
+@pytest.mark.parametrize("name", ["mla", "gla2", "gla2_spec4"])
 def test_scores_far_above_first_tile(name):
     """Scores that grow by far more than 2^64 (log2 units) after the first
     64-key tile: the streaming latent kernel must take its second pass with
