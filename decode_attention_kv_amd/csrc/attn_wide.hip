@@ -29,13 +29,14 @@
 // per step; probabilities alternate between two LDS buffers and one tile
 // is in flight instead of two.
 //
-// LDS layout of a stage (64 banks of 4 bytes, 16 lanes served per cycle):
-// the 16-byte K reads of 16 consecutive keys and the transposing V^T reads
-// (4 keys x 2 16-byte units per 16 lanes) must hit distinct banks.  Latent
-// blocks of 1 KB (one 512-wide row, or two 256-wide rows) sit 1072 bytes
-// apart, a stride of 3 mod 16 units, set by the LDS base of each
-// direct-to-LDS load (one 1 KB load per block); within a two-row block the
-// second row's units are XOR-ed with 8.  RoPE rows are 128 bytes, unpadded,
+// LDS layout of a stage (the LDS serves 256 bytes per clock when a read's
+// lanes hit distinct banks): latent blocks of 1 KB (one 512-wide row, or
+// two 256-wide rows) sit 1056 bytes apart (a stride of 32 mod 64 bytes), set
+// by the LDS base of each direct-to-LDS load (one 1 KB load per block);
+// within a two-row block the second row's units are XOR-ed with 8.  With
+// that stride the 16-byte K reads of 16 consecutive keys and the
+// transposing V^T reads run at the full rate, measured for every operand
+// pattern of this kernel; strides of 0, 16 or 48 mod 64 bytes halve it.  RoPE rows are 128 bytes, unpadded,
 // with units XOR-ed by (row / 2) mod 8.  Every operand address is then one
 // or two per-lane bases plus an immediate offset, and each load needs a
 // single per-lane offset register.
@@ -93,9 +94,9 @@ __device__ __forceinline__ void dma16(const char* base, uint32_t voff, uint32_t 
 template <int DC, int DR> struct Geo {
   static_assert((DC == 256 || DC == 512) && DR == 64, "latent widths");
   static constexpr bool PAIR = DC == 256;    // two latent rows per 1 KB block
-  static constexpr int BSTR = 1072;          // latent block stride (67 units, 3 mod 16)
+  static constexpr int BSTR = 1056;          // latent block stride (32 mod 64 bytes)
   static constexpr int LLOADS = PAIR ? 32 : 64;   // latent blocks (1 KB loads) per stage
-  static constexpr int R_OFF = LLOADS * BSTR + (PAIR ? 512 : 0);  // 1 KB aligned
+  static constexpr int R_OFF = (LLOADS * BSTR + 1023) / 1024 * 1024;  // 1 KB aligned
   static constexpr int RLOADS = 8;           // 64 RoPE rows x 128 bytes
   static constexpr int LOADS = LLOADS + RLOADS;
   static constexpr int STAGE = R_OFF + RLOADS * 1024;
