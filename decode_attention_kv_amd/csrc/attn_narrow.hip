@@ -12,8 +12,9 @@ namespace {
 // keys [16w, 16w + 16).  Each wave streams its slices through a private ring
 // of STAGES LDS buffers filled by direct global->LDS 16-byte loads, so a wave
 // waits only on its own loads (vmcnt) and the main loop has no barriers.
-// Rows are stored with 16-byte chunks XOR-swizzled by the key index so the
-// K-operand reads of 16 keys and the transposing V reads hit distinct banks.
+// Rows are stored with 16-byte chunks XOR-swizzled by a function of the key
+// index (chunk_swz) so the K-operand reads of 16 keys and the transposing V
+// reads hit distinct banks.
 // Per 16-key slice: S^T = K Q^T (MFMA 16x16x32), online softmax, and
 // O^T += V^T P^T with MFMA 16x16x16 whose V^T operand comes from
 // ds_read_b64_tr_b16.  The waves' (max, sum, O) states are merged through
@@ -151,9 +152,22 @@ template <int KIND, int D, int DR> struct Geo {
   static constexpr int LOADS = WAVE_BYTES / 1024;
 };
 
+// 16-byte chunk c of row r of a stage sits at chunk position
+// c ^ chunk_swz(r, CPR).  Rows of 16 chunks (256 bytes, so every row starts
+// at bank 0) swizzle by 2 r: the transposing V reads of a 32-lane group
+// cover 8 rows x 2 chunks, which then hit 16 distinct 16-byte bank groups
+// (swizzling by r puts chunks 2 d and 2 d + 1 of rows r and r ^ 1 on the
+// same banks and halves their rate, measured); rows of 8 chunks (128 bytes,
+// two rows per bank period) swizzle by r.  The K-operand reads of 16 keys
+// run at the full rate with either.
+__device__ __forceinline__ constexpr int chunk_swz(int r, int cpr) {
+  return cpr >= 16 ? (2 * r) & (cpr - 1) : r & (cpr - 1);
+}
+
 // Per-lane byte offsets of the direct-to-LDS loads of one 16-key slice of
 // rows of ROWB bytes: lane l of load i covers row i*RPI + l/CPR at swizzled
-// chunk position l%CPR, i.e. it fetches logical chunk (l%CPR) ^ (row % CPR).
+// chunk position l%CPR, i.e. it fetches logical chunk
+// (l%CPR) ^ chunk_swz(row, CPR).
 // Cache policy of the cache loads: nontemporal (streaming).  Every cache
 // row is read once per call, and the hint raises streaming read bandwidth
 // by about a tenth on gfx950.
@@ -170,7 +184,7 @@ struct SliceDMA {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       row[i] = i * RPI + lane / CPR;
-      const int c = (lane % CPR) ^ (row[i] & (CPR - 1));
+      const int c = (lane % CPR) ^ chunk_swz(row[i], CPR);
       off[i] = (uint32_t)(row[i] * token_stride * 2 + c * 16);
     }
   }
@@ -466,7 +480,7 @@ void decode_narrow(Params p) {
   uint32_t v_off[NDVT];
   {
     const int kl = grp * 4 + (col >> 2);
-    const int sw = kl & (CPR0 - 1);
+    const int sw = chunk_swz(kl, CPR0);
 #pragma unroll
     for (int dt = 0; dt < NDVT; ++dt) {
       const int cidx = 2 * dt + ((col & 3) >> 1);
@@ -480,8 +494,8 @@ void decode_narrow(Params p) {
   for (int c = 0; c < NKC; ++c) {
     const int ch = 4 * c + grp;
     k_off[c] = (KIND == GQA || ch < DN / 8)
-                   ? G::K_OFF + col * G::ROW0 + ((ch ^ (col & (CPR0 - 1))) * 16)
-                   : G::R_OFF + col * G::ROWR + (((ch - DN / 8) ^ (col & (CPRR - 1))) * 16);
+                   ? G::K_OFF + col * G::ROW0 + ((ch ^ chunk_swz(col, CPR0)) * 16)
+                   : G::R_OFF + col * G::ROWR + (((ch - DN / 8) ^ chunk_swz(col, CPRR)) * 16);
   }
 
   // one 16-key slice of tile t, read from stage u
