@@ -882,23 +882,21 @@ int launch_wide_one(Params p, int n_items, hipStream_t stream) {
   const int n_groups = p.h_q / p.g;
   const int units = (n_items + n_groups - 1) / n_groups;   // (sequence, chunk) pairs
   const dim3 grid((units + 7) / 8 * 8 * n_groups * p.row_blocks);
-  // The pipelined schedule holds one tile in flight instead of two but
-  // needs one barrier per tile instead of two: faster where the workgroup
-  // is bound by its MFMA and LDS work and several row blocks share each
-  // tile through the L2 (groups of more than 64 rows: speculative and
-  // multi-token decode), slower for a single row block, which streams from
-  // HBM.
-  bool launched = false;
-  if constexpr (DC == 256 && RT >= 2 && S == 3 && !SP) {
-    if (RT == 4 || p.row_blocks > 1) {
-      hipLaunchKernelGGL((wide::decode_wide<DC, DR, RT, S, KQ, false, SP, true>), grid,
-                         dim3(2 * KQ * 64), 0, stream, p);
-      launched = true;
-    }
-  }
-  if (!launched)
+  // 128-row workgroups run the pipelined schedule: it holds one tile in
+  // flight instead of two but needs one barrier per tile instead of two,
+  // and interleaves the softmax into the P V MFMAs, which a single wave per
+  // SIMD needs (measured against the plain schedule with 64-row workgroups:
+  // +31 % at q_len 4; with 64-row workgroups the pipelined form gained 12 %
+  // at q_len 4 and lost 3-7 % at q_len 1, where one tile in flight is too
+  // little to stream from HBM).
+  if constexpr (RT == 4) {
+    static_assert(DC == 256 && S == 3 && !SP, "128-row workgroups: 256-wide, whole tiles");
+    hipLaunchKernelGGL((wide::decode_wide<DC, DR, RT, S, KQ, false, SP, true>), grid,
+                       dim3(2 * KQ * 64), 0, stream, p);
+  } else {
     hipLaunchKernelGGL((wide::decode_wide<DC, DR, RT, S, KQ, false, SP, false>), grid,
                        dim3(2 * KQ * 64), 0, stream, p);
+  }
   // fix-up pass: exits at once unless the first pass flagged the workgroup
   hipLaunchKernelGGL((wide::decode_wide<DC, DR, RT, S, KQ, true, SP, false>), grid,
                      dim3(2 * KQ * 64), 0, stream, p);

@@ -76,6 +76,17 @@ SMALL = {
                         seqlen_hi=300, max_seqlen=320),
     "gla4_h12": small("gla2", batch=3, h_q=12, groups=4, seqlen_lo=1, seqlen_hi=400,
                       max_seqlen=448),
+    # 256-wide latent groups of more than 64 rows (128-row workgroups, the
+    # pipelined schedule): 68 rows (the second row half holds 4), 96 rows,
+    # 192 rows (a full and a half-empty workgroup), 512 rows
+    "gla2_h68_q2": small("gla2", batch=2, h_q=68, q_len=2, causal=True, seqlen_lo=2,
+                         seqlen_hi=500, max_seqlen=512),
+    "gla2_h96_q2": small("gla2", batch=3, h_q=96, q_len=2, causal=True, seqlen_lo=2,
+                         seqlen_hi=400, max_seqlen=448),
+    "gla2_q3": small("gla2", batch=2, q_len=3, causal=True, seqlen_lo=3, seqlen_hi=600,
+                     max_seqlen=640),
+    "gla2_q8": small("gla2", batch=2, q_len=8, causal=True, seqlen_lo=8, seqlen_hi=300,
+                     max_seqlen=320),
     # paired GTA groups: three pairs, and groups of 4 rows (half a row tile)
     "gta_h6": small("gta_8k", batch=2, h_q=48, groups=6, seqlen_lo=1, seqlen_hi=700,
                     max_seqlen=704),
