@@ -409,9 +409,12 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
   // scores S^T of this wave's KPW keys of the tile at stage base sb: MT M
   // tiles x RT row tiles.  The K operand reads run KD steps ahead of the
   // MFMAs that consume them (scheduling fences keep that order); when
-  // `spread`, load k of the fetch nf is issued after step 2 k + 1.
-  auto score_phase = [&](const char* sb, const auto& nf, bool spread,
-                         f32x4 (&sa)[RT][MT]) __attribute__((always_inline)) {
+  // `spread` (a compile-time flag: a branch around each load cost a lone
+  // wave per SIMD about 7 % at q_len 4), load k of the fetch nf is issued
+  // after step 2 k + 1.
+  auto score_phase_c = [&](const char* sb, const auto& nf, auto spread_c,
+                           f32x4 (&sa)[RT][MT]) __attribute__((always_inline)) {
+    constexpr bool spread = decltype(spread_c)::value;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -449,6 +452,13 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+  };
+  auto score_phase = [&](const char* sb, const auto& nf, bool spread,
+                         f32x4 (&sa)[RT][MT]) __attribute__((always_inline)) {
+    if (spread)
+      score_phase_c(sb, nf, std::true_type{}, sa);
+    else
+      score_phase_c(sb, nf, std::false_type{}, sa);
   };
 
   // x = scale * score + nm (log2 units); lane holds keys
