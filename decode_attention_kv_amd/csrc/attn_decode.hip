@@ -9,6 +9,7 @@
 // (Hydragen's decomposition on the "Efficient Inference" tag page).
 #include "attn_device.h"
 
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 
@@ -102,20 +103,56 @@ int resident_slots(int per_cu) {
 
 // the plan's device arrays, or a plan to pass in the launch arguments
 bool plan_on_device(const attn_plan_t* plan) { return plan->items && plan->seqinfo; }
-bool plan_inline(const attn_plan_t* plan) {
-  return !plan->items && !plan->seqinfo && plan->inline_ok && plan->items_host &&
-         plan->seqinfo_host && plan->n_groups > 0 &&
-         4 * (int64_t)plan->batch + plan->n_items / plan->n_groups <= ATTN_PLAN_INLINE_MAX;
+// The launch-argument form of a host plan: 0 (none), 1 (an int32 per
+// chunk) or 2 (half an int32 per chunk).
+int inline_form(const attn_plan_t* plan) {
+  if (plan->items || plan->seqinfo || !plan->inline_ok || !plan->items_host ||
+      !plan->seqinfo_host || plan->n_groups <= 0 || plan->batch >= 65536)
+    return 0;
+  // the packed fields: split count and chunk length in tiles, 16 bits each
+  int max_splits = 1;
+  for (int b = 0; b < plan->batch; ++b) {
+    const int32_t* si = plan->seqinfo_host + 4 * (int64_t)b;
+    if (si[0] < 1 || si[0] >= 65536 || si[3] <= 0 || si[3] % 64 || (si[3] >> 6) >= 65536)
+      return 0;
+    max_splits = std::max(max_splits, (int)si[0]);
+  }
+  const int64_t chunks = plan->n_items / plan->n_groups;
+  const bool half = plan->batch <= 2048 && max_splits <= 32;
+  if (3 * (int64_t)plan->batch + (half ? (chunks + 1) / 2 : chunks) > ATTN_PLAN_INLINE_MAX)
+    return 0;
+  return half ? 2 : 1;
 }
-// compact copy of a host plan into the launch arguments
+bool plan_inline(const attn_plan_t* plan) { return inline_form(plan) != 0; }
+// compact copy of a host plan into the launch arguments: per sequence
+// n_splits | (chunk / 64) << 16, the partial slot base and L; per chunk
+// b | split << 16 (form 1), or b | split << 11 in 16 bits, two per int32
+// (form 2)
 void pack_inline(Params& p, const attn_plan_t* plan) {
-  p.plan_inline = 1;
+  const int form = inline_form(plan);
+  p.plan_inline = form;
   p.inl_batch = plan->batch;
-  std::memcpy(p.inl, plan->seqinfo_host, sizeof(int32_t) * 4 * plan->batch);
+  for (int b = 0; b < plan->batch; ++b) {
+    const int32_t* si = plan->seqinfo_host + 4 * (int64_t)b;
+    p.inl[3 * b + 0] = (int32_t)((uint32_t)si[0] | ((uint32_t)(si[3] >> 6) << 16));
+    p.inl[3 * b + 1] = si[1];
+    p.inl[3 * b + 2] = si[2];
+  }
   const int g = plan->n_groups;
-  for (int c = 0; c < plan->n_items / g; ++c) {
-    const int32_t* it = plan->items_host + 4 * (int64_t)c * g;
-    p.inl[4 * plan->batch + c] = (int32_t)((uint32_t)it[0] | ((uint32_t)it[2] << 16));
+  const int n_chunks = plan->n_items / g;
+  int32_t* const ce = p.inl + 3 * plan->batch;
+  if (form == 2) {
+    for (int w = 0; w < (n_chunks + 1) / 2; ++w) ce[w] = 0;
+    for (int c = 0; c < n_chunks; ++c) {
+      const int32_t* it = plan->items_host + 4 * (int64_t)c * g;
+      const uint32_t e = (uint32_t)it[0] | ((uint32_t)it[2] << 11);
+      ce[c >> 1] = (int32_t)((uint32_t)ce[c >> 1] | (e << (16 * (c & 1))));
+    }
+  } else {
+    for (int c = 0; c < n_chunks; ++c) {
+      const int32_t* it = plan->items_host + 4 * (int64_t)c * g;
+      ce[c] = (int32_t)((uint32_t)it[0] | ((uint32_t)it[2] << 16));
+    }
   }
 }
 

@@ -57,9 +57,11 @@ struct Params {
   // RoPE: revolutions per position of frequency k as hi + lo floats
   float rope_hi[kMaxRope / 2];
   float rope_lo[kMaxRope / 2];
-  // plan in the launch arguments (plan_inline = 1): inl[4 b .. 4 b + 3] =
-  // n_splits, partial slot base, L, chunk of sequence b; inl[4 inl_batch +
-  // c] = b | split << 16 of chunk c, whose groups are items c * groups + j
+  // plan in the launch arguments (plan_inline = 1 or 2): inl[3 b .. 3 b + 2]
+  // = n_splits | (chunk / 64) << 16, partial slot base, L of sequence b;
+  // chunk c (whose groups are items c * groups + j) is inl[3 inl_batch + c]
+  // = b | split << 16 (form 1), or the 16-bit b | split << 11 in half c % 2
+  // of inl[3 inl_batch + c / 2] (form 2)
   int32_t plan_inline;
   int32_t inl_batch;
   int32_t inl[ATTN_PLAN_INLINE_MAX];
@@ -72,20 +74,37 @@ struct PlanItem {
 };
 __device__ __forceinline__ void seq_info(const Params& p, int b, int& n_splits, int& slot_base,
                                          int& L, int& chunk) {
-  const int32_t* si = p.plan_inline ? p.inl + 4 * b : p.seqinfo + 4 * b;
-  n_splits = __builtin_amdgcn_readfirstlane(si[0]);
-  slot_base = __builtin_amdgcn_readfirstlane(si[1]);
-  L = __builtin_amdgcn_readfirstlane(si[2]);
-  chunk = __builtin_amdgcn_readfirstlane(si[3]);
+  if (p.plan_inline) {
+    const int32_t* si = p.inl + 3 * b;
+    const uint32_t w0 = (uint32_t)__builtin_amdgcn_readfirstlane(si[0]);
+    n_splits = (int)(w0 & 0xffffu);
+    chunk = (int)(w0 >> 16) << 6;
+    slot_base = __builtin_amdgcn_readfirstlane(si[1]);
+    L = __builtin_amdgcn_readfirstlane(si[2]);
+  } else {
+    const int32_t* si = p.seqinfo + 4 * b;
+    n_splits = __builtin_amdgcn_readfirstlane(si[0]);
+    slot_base = __builtin_amdgcn_readfirstlane(si[1]);
+    L = __builtin_amdgcn_readfirstlane(si[2]);
+    chunk = __builtin_amdgcn_readfirstlane(si[3]);
+  }
 }
 __device__ __forceinline__ PlanItem load_item(const Params& p, int item) {
   PlanItem r;
   if (p.plan_inline) {
     const int n_groups = p.h_q / p.g;
     const int c = item / n_groups;
-    const uint32_t e = (uint32_t)__builtin_amdgcn_readfirstlane(p.inl[4 * p.inl_batch + c]);
-    r.b = (int)(e & 0xffffu);
-    r.split = (int)(e >> 16);
+    if (p.plan_inline == 2) {
+      const uint32_t w =
+          (uint32_t)__builtin_amdgcn_readfirstlane(p.inl[3 * p.inl_batch + (c >> 1)]);
+      const uint32_t e = (c & 1) ? (w >> 16) : (w & 0xffffu);
+      r.b = (int)(e & 0x7ffu);
+      r.split = (int)(e >> 11);
+    } else {
+      const uint32_t e = (uint32_t)__builtin_amdgcn_readfirstlane(p.inl[3 * p.inl_batch + c]);
+      r.b = (int)(e & 0xffffu);
+      r.split = (int)(e >> 16);
+    }
     r.j = item - c * n_groups;
   } else {
     const int32_t* it = p.items + 4 * item;

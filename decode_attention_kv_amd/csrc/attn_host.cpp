@@ -251,7 +251,15 @@ int attn_decode_plan(const attn_shape_t* shape, const int32_t* seqlens_host, int
   plan->queue = nullptr;
   plan->items_host = items_host;
   plan->seqinfo_host = seqinfo_host;
-  plan->inline_ok = (4 * (int64_t)batch + (int64_t)chunks.size() <= ATTN_PLAN_INLINE_MAX &&
+  // launch-argument form: three int32 per sequence (the split count and
+  // the chunk length in tiles share one) and one per chunk, or half of one
+  // (sequence in 11 bits, split in 5) for batches of at most 2048 sequences
+  // split at most 32 ways
+  const bool half = batch <= 2048 && max_splits <= 32;
+  const int64_t chunk_words =
+      half ? ((int64_t)chunks.size() + 1) / 2 : (int64_t)chunks.size();
+  plan->inline_ok = (3 * (int64_t)batch + chunk_words <= ATTN_PLAN_INLINE_MAX &&
+                     ct < 65536 &&
                      batch < 65536 && max_splits < 65536)
                         ? 1
                         : 0;

@@ -174,10 +174,11 @@ typedef struct {
  */
 
 /*
- * Launch-argument plans.  A plan needs 4 * batch + n_items / n_groups int32
- * in compact form (the sequences' info and one entry per chunk); when that
- * is at most ATTN_PLAN_INLINE_MAX (and batch and n_splits_b stay below
- * 65536), attn_decode_plan sets inline_ok.  A decode or merge call whose
+ * Launch-argument plans.  A plan needs 3 * batch + n_items / n_groups int32
+ * in compact form (three per sequence, one per chunk; half an int32 per
+ * chunk when batch <= 2048 and every n_splits_b <= 32); when that is at
+ * most ATTN_PLAN_INLINE_MAX (and batch and n_splits_b stay below 65536 and
+ * every chunk below 2^22 tokens), attn_decode_plan sets inline_ok.  A decode or merge call whose
  * plan then has items == NULL and seqinfo == NULL packs the plan from
  * items_host / seqinfo_host (which must still hold what attn_decode_plan
  * wrote) into the kernels' launch arguments, so no upload is needed.  With

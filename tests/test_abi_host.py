@@ -410,13 +410,33 @@ def test_append_rejects_bad_arguments(case):
 
 
 def test_launch_argument_plan_capacity():
-    # 4 * batch + chunks int32 must fit ATTN_PLAN_INLINE_MAX
+    # 3 * batch + chunks int32 must fit ATTN_PLAN_INLINE_MAX
     st, plan, items, info = _plan([5000, 100, 7], groups=8, h_q=32)
     chunks = plan.n_items // plan.n_groups
-    assert plan.inline_ok == 1 and 4 * 3 + chunks <= binding.ATTN_PLAN_INLINE_MAX
+    assert plan.inline_ok == 1 and 3 * 3 + chunks <= binding.ATTN_PLAN_INLINE_MAX
     assert plan.items_host and plan.seqinfo_host
-    st, plan, _, _ = _plan([8192] * 200, groups=8, h_q=32)      # 800 + chunks > 800
+    st, plan, _, _ = _plan([8192] * 200, groups=8, h_q=32)      # 600 + 200 chunks fit
+    assert plan.inline_ok == 1 and plan.n_items // plan.n_groups <= 200
+    st, plan, _, _ = _plan([8192] * 267, groups=8, h_q=32)      # 801 + chunks > 800
     assert plan.inline_ok == 0
+
+
+def test_launch_argument_plan_half_word_chunks():
+    # batches of at most 2048 sequences split at most 32 ways take half an
+    # int32 per chunk: 3 * 128 + 400 chunks = 784 words in the full form,
+    # 3 * 128 + 200 in the half form; 3 * 200 + 400 does not fit either
+    lens = [4096] * 128
+    st, plan, items, info = _plan(lens, groups=1, h_q=16, chunk=1024)
+    chunks = plan.n_items // plan.n_groups
+    assert st == binding.ATTN_OK and chunks == 512 and plan.max_splits == 4
+    assert 3 * 128 + chunks > binding.ATTN_PLAN_INLINE_MAX   # full form would not fit
+    assert plan.inline_ok == 1                                  # half form: 640 words
+    st, plan, _, _ = _plan([4096] * 200, groups=1, h_q=16, chunk=512)
+    assert plan.max_splits == 8 and 3 * 200 + plan.n_items // 2 > binding.ATTN_PLAN_INLINE_MAX
+    assert plan.inline_ok == 0
+    # more than 32 splits: full-width chunk entries only
+    st, plan, _, _ = _plan([64 * 40] * 4, groups=1, h_q=16, chunk=64)
+    assert plan.max_splits == 40 and plan.inline_ok == 1        # 12 + 160 words
 
 
 @pytest.mark.parametrize("kind", ["gqa", "gta", "latent"])

@@ -552,6 +552,36 @@ def test_launch_argument_plan_matches_device_plan(name, page_size):
     assert torch.equal(o1, o3) and torch.equal(l1, l3)
 
 
+# launch-argument forms: full-width chunk entries (a sequence split more
+# than 32 ways) and half-word ones (an odd chunk count included)
+@pytest.mark.parametrize("name,lo,hi,form", [("gqa_llama8b", 4000, 4160, 1), ("mla", 2200, 2500, 1),
+                                             ("gla2_spec4", 2100, 2200, 1),
+                                             ("gqa_llama8b", 100, 700, 2), ("gla2", 300, 900, 2)])
+def test_launch_argument_plan_forms(name, lo, hi, form):
+    """Plans packed into the launch arguments with full-width or half-word
+    chunk entries give the device plan's results bit for bit, for the
+    decode and for a deferred merge."""
+    w = SMALL[name].with_(batch=3, seqlen_lo=lo, seqlen_hi=hi, max_seqlen=hi + 64)
+    d = H.to_device(w, synth.make_inputs(w))
+    o1, l1, plan1 = H.run(w, d, chunk_tokens=64)
+    chunks = plan1.plan.n_items // plan1.plan.n_groups
+    print(f"[inline form] {name} splits={plan1.plan.max_splits} chunks={chunks}", flush=True)
+    assert (plan1.plan.max_splits > 32) == (form == 1)
+    if form == 2:
+        assert chunks % 2 == 1 or name != "gla2"   # the last half word half used
+    o2, l2, plan2 = H.run(w, d, chunk_tokens=64, inline_plan=True)
+    assert plan2.plan.items is None and plan2.plan.seqinfo is None
+    o3, l3, plan3, ws = binding.decode(
+        w.kind, d["q"], d["pool0"], d["pool1"], d["rope"], d["page_table"], d["seqlens"],
+        d["seqlens_host"], groups=w.groups, scale=w.softmax_scale, causal=w.causal,
+        rope_theta=w.rope_theta, d_rope=w.d_rope, chunk_tokens=64, defer_merge=True,
+        inline_plan=True)
+    binding.merge(plan3, o3, l3, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.equal(o1, o3) and torch.equal(l1, l3)
+
+
 def w_pages_ok(name):
     # fp32 shapes run on the general kernel at their own page size
     return SMALL[name].dtype == "bf16"
