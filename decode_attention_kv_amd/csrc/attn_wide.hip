@@ -8,8 +8,9 @@
 // ring of STAGES 64-key LDS stages filled by direct global->LDS loads.
 // Configurations (RT, KQ): 256-wide latents (2, 4), eight waves two per
 // SIMD, or (4, 2) for groups of more than 64 rows, four waves of 64 rows
-// each, which halves the LDS operand bytes per row (the bound of this
-// kernel at high intensity); 512-wide latents (2, 2).
+// each (one per SIMD), which halves the LDS operand bytes per row and
+// doubles the MFMAs per operand read; 512-wide latents (2, 2), one wave per
+// SIMD.
 //
 // Work split inside a workgroup of 2 KQ waves: wave (kq, rh) owns the row
 // half rh (16*RT rows) and
@@ -36,10 +37,10 @@
 // within a two-row block the second row's units are XOR-ed with 8.  With
 // that stride the 16-byte K reads of 16 consecutive keys and the
 // transposing V^T reads run at the full rate, measured for every operand
-// pattern of this kernel; strides of 0, 16 or 48 mod 64 bytes halve it.  RoPE rows are 128 bytes, unpadded,
-// with units XOR-ed by (row / 2) mod 8.  Every operand address is then one
-// or two per-lane bases plus an immediate offset, and each load needs a
-// single per-lane offset register.
+// pattern of this kernel; strides of 0, 16 or 48 mod 64 bytes halve it.
+// RoPE rows are 128 bytes, unpadded, with units XOR-ed by (row / 2) mod 8.
+// Every operand address is then one or two per-lane bases plus an
+// immediate offset, and each load needs a single per-lane offset register.
 //
 // Softmax: every row keeps a fixed reference max m_ref, the pair-wide max
 // of its first tile (the visible keys of a chunk are a prefix of it, so
@@ -114,25 +115,25 @@ constexpr int PT_MAX = 512;  // tiles whose page ids are kept in LDS
 
 // LDS of a workgroup: the ring, one probability buffer (two for the
 // pipelined schedule) and the page-id table
-template <int DC, int RT, int STAGES, bool PIPE> constexpr int wide_lds_bytes() {
-  return STAGES * Geo<DC, 64>::STAGE + (PIPE ? 2 : 1) * 4 * RT * 1024 + PT_MAX * 4;
+template <int DC, int RT, int STAGES, bool PIPE, int RH = 2> constexpr int wide_lds_bytes() {
+  return STAGES * Geo<DC, 64>::STAGE + (PIPE ? 2 : 1) * RH * 2 * RT * 1024 + PT_MAX * 4;
 }
 
 // Stream the item's chunk and write its output rows; returns true, writing
 // nothing, when (RESCALE = false) some row outgrew its fixed reference.
-template <int DC, int DR, int RT, int STAGES, int KQ, bool RESCALE, bool SP, bool PIPE>
+template <int DC, int DR, int RT, int STAGES, int KQ, bool RESCALE, bool SP, bool PIPE, int RH>
 __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* ring) {
   using G = Geo<DC, DR>;
-  constexpr int NW = 2 * KQ;           // waves: key part kq = wave % KQ, row half wave / KQ
+  constexpr int NW = RH * KQ;          // waves: key part kq = wave % KQ, row part wave / KQ
   constexpr int KPW = 64 / KQ;         // keys per wave per tile
   constexpr int MT = KPW / 16;         // 16-key M tiles per wave
   constexpr int NDVW = DC / 16 / KQ;   // 16-wide value tiles per wave
   static_assert(KQ == 2 || KQ == 4, "key split");
   static_assert(G::LLOADS % NW == 0 && G::RLOADS % NW == 0, "loads split evenly over the waves");
   constexpr int LPW = G::LOADS / NW;   // loads per wave per stage
-  constexpr int R_WG = 32 * RT;        // rows per workgroup
+  constexpr int R_WG = 16 * RT * RH;   // rows per workgroup
   constexpr int PBUF = STAGES * G::STAGE;
-  constexpr int PTAB = PBUF + (PIPE ? 2 : 1) * 4 * RT * 1024;   // page-id table
+  constexpr int PTAB = PBUF + (PIPE ? 2 : 1) * RH * 2 * RT * 1024;   // page-id table
   // small pages: wave w loads the rows of keys [KR w, KR w + KR) of a tile;
   // their page ids sit in a ring of STAGES slots of NW x 64 bytes at PTAB
   constexpr int KR = 64 / NW;
@@ -672,7 +673,7 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
     // i - 1 (P V) and stage (i + 1) % 3 receives tile i + 1, issued over the
     // score MFMAs of step i.  Probabilities alternate between two buffers.
     static_assert(DC == 256 && STAGES == 3 && !SP && !RESCALE, "pipelined schedule");
-    constexpr int PBS = 4 * RT * 1024;
+    constexpr int PBS = RH * 2 * RT * 1024;
     // page id of tile t (clamped to the last tile) from the LDS table, read
     // a step before use; tiles past the table read the page table at use
     auto page_of = [&](int t) __attribute__((always_inline)) {
@@ -834,14 +835,16 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
 // RESCALE = false: the fixed-reference pass; records per workgroup whether
 // it had to give up (flags[block]).  RESCALE = true: the fix-up pass, a
 // second launch over the same grid that only works where the flag is set.
-// PIPE: the pipelined tile schedule (fixed-reference pass only).
-template <int DC, int DR, int RT, int STAGES, int KQ, bool RESCALE, bool SP, bool PIPE>
-__global__ __launch_bounds__(2 * KQ * 64) __attribute__((amdgpu_waves_per_eu(KQ / 2, KQ / 2)))
+// PIPE: the pipelined tile schedule (fixed-reference pass only).  RH row
+// parts x KQ key parts = RH KQ waves, RH KQ / 4 per SIMD.
+template <int DC, int DR, int RT, int STAGES, int KQ, bool RESCALE, bool SP, bool PIPE, int RH>
+__global__ __launch_bounds__(RH * KQ * 64)
+__attribute__((amdgpu_waves_per_eu(RH * KQ / 4, RH * KQ / 4)))
 void decode_wide(Params p) {
   using G = Geo<DC, DR>;
-  constexpr int LDS = wide_lds_bytes<DC, RT, STAGES, PIPE>();
+  constexpr int LDS = wide_lds_bytes<DC, RT, STAGES, PIPE, RH>();
   static_assert(LDS <= 160 * 1024, "LDS");
-  static_assert((STAGES - 2) * (G::LOADS / (2 * KQ) + 1) <= 63, "vmcnt range");
+  static_assert((STAGES - 2) * (G::LOADS / (RH * KQ) + 1) <= 63, "vmcnt range");
   static_assert(STAGES == 2 || STAGES == 3, "tile loop unrolled for 2 or 3 stages");
   __shared__ __attribute__((aligned(1024))) char ring[LDS];
 
@@ -877,7 +880,7 @@ void decode_wide(Params p) {
   itm.t_end = min(itm.t0 + chunk, itm.L);
   itm.n_tiles = (itm.t_end - itm.t0 + 63) / 64;
 
-  const bool gave_up = stream<DC, DR, RT, STAGES, KQ, RESCALE, SP, PIPE>(p, itm, ring);
+  const bool gave_up = stream<DC, DR, RT, STAGES, KQ, RESCALE, SP, PIPE, RH>(p, itm, ring);
   if constexpr (!RESCALE) {
     if (threadIdx.x == 0) p.flags[blockIdx.x] = gave_up ? 1 : 0;
   }
@@ -885,10 +888,15 @@ void decode_wide(Params p) {
 
 }  // namespace wide
 
-template <int DC, int DR, int RT, int S, int KQ, bool SP>
+// RH row parts of RT row tiles (16 RT RH rows per workgroup), KQ key parts.
+// The fix-up pass runs the same grid with two row halves of RH RT / 2 row
+// tiles (the same rows per workgroup).
+template <int DC, int DR, int RT, int S, int KQ, bool SP, int RH = 2>
 int launch_wide_one(Params p, int n_items, hipStream_t stream) {
+  static_assert(RH == 2 || (RH == 4 && RT == 1), "row parts");
+  constexpr int RTF = RT * RH / 2;   // row tiles per wave of the fix-up pass
   p.n_items = n_items;
-  p.row_blocks = (p.rows + 32 * RT - 1) / (32 * RT);
+  p.row_blocks = (p.rows + 16 * RT * RH - 1) / (16 * RT * RH);
   const int n_groups = p.h_q / p.g;
   const int units = (n_items + n_groups - 1) / n_groups;   // (sequence, chunk) pairs
   const dim3 grid((units + 7) / 8 * 8 * n_groups * p.row_blocks);
@@ -901,14 +909,14 @@ int launch_wide_one(Params p, int n_items, hipStream_t stream) {
   // little to stream from HBM).
   if constexpr (RT == 4) {
     static_assert(DC == 256 && S == 3 && !SP, "128-row workgroups: 256-wide, whole tiles");
-    hipLaunchKernelGGL((wide::decode_wide<DC, DR, RT, S, KQ, false, SP, true>), grid,
-                       dim3(2 * KQ * 64), 0, stream, p);
+    hipLaunchKernelGGL((wide::decode_wide<DC, DR, RT, S, KQ, false, SP, true, RH>), grid,
+                       dim3(RH * KQ * 64), 0, stream, p);
   } else {
-    hipLaunchKernelGGL((wide::decode_wide<DC, DR, RT, S, KQ, false, SP, false>), grid,
-                       dim3(2 * KQ * 64), 0, stream, p);
+    hipLaunchKernelGGL((wide::decode_wide<DC, DR, RT, S, KQ, false, SP, false, RH>), grid,
+                       dim3(RH * KQ * 64), 0, stream, p);
   }
   // fix-up pass: exits at once unless the first pass flagged the workgroup
-  hipLaunchKernelGGL((wide::decode_wide<DC, DR, RT, S, KQ, true, SP, false>), grid,
+  hipLaunchKernelGGL((wide::decode_wide<DC, DR, RTF, S, KQ, true, SP, false, 2>), grid,
                      dim3(2 * KQ * 64), 0, stream, p);
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
@@ -932,6 +940,16 @@ int launch_wide_sp(const Params& p, int n_items, hipStream_t stream) {
   } else {
     if (attn_internal::wide_rt(DC, p.rows) == 1)
       return launch_wide_one<DC, DR, 1, S, KQ, SP>(p, n_items, stream);
+    // 512-wide latents with 33-128 rows on pages under 64 tokens: four row
+    // parts of one row tile (eight waves, two per SIMD) instead of two of
+    // two (four waves, one per SIMD), the same 64 rows per workgroup; more
+    // waves issue the per-row loads (MLA at q_len 1, pages of 1 / 4 / 16
+    // tokens: +4 to +7 %).  With whole-tile pages, or more rows (q_len 4:
+    // -2.5 % at pages of 16), the eight waves' doubled K and V operand reads
+    // cost more than their overlap gains (-2 % to -5 %).
+    if constexpr (DC >= 512 && SP) {
+      if (p.rows <= 128) return launch_wide_one<DC, DR, 1, S, KQ, SP, 4>(p, n_items, stream);
+    }
     return launch_wide_one<DC, DR, 2, S, KQ, SP>(p, n_items, stream);
   }
 }
