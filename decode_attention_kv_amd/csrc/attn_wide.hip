@@ -6,22 +6,22 @@
 // holds 32*RT query rows of a group (the group's heads times the query
 // tokens, or a block of them) and streams the rows of its chunk through a
 // ring of STAGES 64-key LDS stages filled by direct global->LDS loads.
-// Configurations (RT, KQ): 256-wide latents (2, 4), eight waves two per
-// SIMD, or (4, 2) for groups of more than 64 rows, four waves of 64 rows
-// each (one per SIMD), which halves the LDS operand bytes per row and
-// doubles the MFMAs per operand read; 512-wide latents (2, 2), one wave per
-// SIMD.
+// Configurations (RT row tiles per wave, KQ key parts, RH row parts):
+// 256-wide latents (2, 4, 2), eight waves two per SIMD, or (4, 2, 2) for
+// groups of more than 64 rows, four waves of 64 rows each (one per SIMD),
+// which halves the LDS operand bytes per row and doubles the MFMAs per
+// operand read; 512-wide latents (2, 2, 2), one wave per SIMD, or on small
+// pages (1, 2, 4), eight waves two per SIMD.
 //
-// Work split inside a workgroup of 2 KQ waves: wave (kq, rh) owns the row
-// half rh (16*RT rows) and
+// Work split inside a workgroup of RH KQ waves: wave (kq, rh) owns the row
+// part rh (16*RT rows) and
 //   * scores S^T = K Q^T for key part kq of every tile (64 / KQ keys; its
 //     rows' queries stay in registers as MFMA B operands),
 //   * O^T += V^T P^T for the value-column part kq of its rows over all 64
 //     keys of the tile; the probabilities of the other key parts come from
 //     the partner waves (kq', rh) through a small LDS buffer.
-// So every K element is read from LDS by two waves (one per row half) and
-// every V element by two (one per row half), half of what a split over rows
-// alone needs.
+// So every K element is read from LDS by RH waves (one per row part) and
+// every V element by RH, against 2 KQ for a split over rows alone.
 //
 // Tile schedules.  Plain: per tile, wait for its stage, scores, softmax,
 // exchange barrier, P V.  Pipelined (256-wide latents, groups of more than
