@@ -602,10 +602,23 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
   };
   const auto no_hook = [](int) __attribute__((always_inline)) {};
 
+  // page id of tile t (clamped to the last tile) from the LDS table, read
+  // a tile (or step) before use, so that no LDS wait follows the barrier;
+  // tiles past the table read the page table at use
+  auto page_of = [&](int t) __attribute__((always_inline)) {
+    return ptab[min(min(t, n_tiles - 1), PT_MAX - 1)];
+  };
+  auto page_at = [&](int t, int pid) __attribute__((always_inline)) {
+    const int tn = min(t, n_tiles - 1);
+    return tn < PT_MAX ? (int64_t)__builtin_amdgcn_readfirstlane(pid)
+                       : (int64_t)sload_i32(pt_row + ((t0 + tn * 64) >> p.page_shift));
+  };
   if constexpr (!PIPE) {
+    int pid = 0;
     if (n_tiles > 0) {
 #pragma unroll
       for (int u = 0; u < STAGES - 1; ++u) issue(u, u);
+      if constexpr (!SP) pid = page_of(STAGES - 1);
     }
 
     // One tile in stage U; when U is a compile-time constant every LDS
@@ -625,10 +638,14 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
       // now (small pages: always spread, after the page ids of tile
       // t + 2 STAGES - 2)
       const auto nf = [&]() __attribute__((always_inline)) {
-        if constexpr (SP)
+        if constexpr (SP) {
           return prepare_sp(t + STAGES - 1, (U + STAGES - 1) % STAGES);
-        else
-          return prepare(t + STAGES - 1, (U + STAGES - 1) % STAGES);
+        } else {
+          const Fetch f = prepare_page(t + STAGES - 1, (U + STAGES - 1) % STAGES,
+                                       page_at(t + STAGES - 1, pid));
+          pid = page_of(t + STAGES);
+          return f;
+        }
       }();
       bool spread = true;
       if constexpr (SP) {
@@ -674,11 +691,6 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
     // score MFMAs of step i.  Probabilities alternate between two buffers.
     static_assert(DC == 256 && STAGES == 3 && !SP && !RESCALE, "pipelined schedule");
     constexpr int PBS = RH * 2 * RT * 1024;
-    // page id of tile t (clamped to the last tile) from the LDS table, read
-    // a step before use; tiles past the table read the page table at use
-    auto page_of = [&](int t) __attribute__((always_inline)) {
-      return ptab[min(min(t, n_tiles - 1), PT_MAX - 1)];
-    };
     int pid = 0;
     auto step = [&](int i, auto ucst) __attribute__((always_inline)) {
       const int U = static_cast<int>(ucst);
@@ -688,10 +700,7 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
       __syncthreads();
       const bool more = i + 1 < n_tiles;
-      const int tn = min(i + 1, n_tiles - 1);
-      const int64_t page = tn < PT_MAX ? __builtin_amdgcn_readfirstlane(pid)
-                                       : sload_i32(pt_row + ((t0 + tn * 64) >> p.page_shift));
-      const Fetch nf = prepare_page(i + 1, (U + 1) % 3, page);
+      const Fetch nf = prepare_page(i + 1, (U + 1) % 3, page_at(i + 1, pid));
       pid = page_of(i + 2);
       const bool spread = more && nf.valid == 64;
       if (more && !spread) issue_clamped(nf);
