@@ -87,6 +87,12 @@ inline bool env_narrow_rt4() {
   static const bool v = env_int("ATTN_NARROW_RT4", 0) != 0;
   return v;
 }
+// Groups of 33-64 rows on pages of 16 tokens or more: one workgroup of two
+// row halves sharing one ring (ATTN_NARROW_HALVES=0: two 32-row workgroups)
+inline bool narrow_row_halves(bool whole_slices) {
+  static const bool v = env_int("ATTN_NARROW_HALVES", 1) != 0;
+  return v && whole_slices && !env_narrow_rt4();
+}
 inline bool env_force_general() {
   static const bool v = env_int("ATTN_FORCE_GENERAL", 0) != 0;
   return v;
@@ -138,9 +144,19 @@ inline KernelChoice choose_kernel(const attn_shape_t& sh) {
     const int lds = k.stages * narrow_stage_bytes(sh.kind, sh.head_dim, sh.d_rope) + 2048;
     int w = 163840 / lds;
     k.wgs_per_cu = w < 1 ? 1 : w > 2 ? 2 : w;
-    // more than 32 rows: two workgroups of 32 rows on one XCD (the second
-    // reads the item's rows from its L2), each as a group of 32 rows
-    if (k.rows > 32 && !env_narrow_rt4()) k.row_blocks = (k.rows + 31) / 32;
+    // more than 32 rows on pages of 16 tokens or more: one workgroup of two
+    // row halves that share one ring, as deep as the LDS holds; else two
+    // workgroups of 32 rows on one XCD (the second reads the item's rows
+    // from its L2), each as a group of 32 rows
+    if (k.rows > 32 && narrow_row_halves(sh.page_size >= 16)) {
+      k.wgs_per_cu = 1;
+      if (env_stages() == 0) {
+        const int s = (163840 - 4096) / narrow_stage_bytes(sh.kind, sh.head_dim, sh.d_rope);
+        k.stages = s < 2 ? 2 : s > 6 ? 6 : s;
+      }
+    } else if (k.rows > 32 && !env_narrow_rt4()) {
+      k.row_blocks = (k.rows + 31) / 32;
+    }
     // with ATTN_NARROW_RT4=1, four row tiles per wave: one wave per SIMD,
     // and on pages of 16 tokens or more a shallower ring, which frees
     // registers for the row tiles (GTA: 2 stages, measured +6 % over 5 at

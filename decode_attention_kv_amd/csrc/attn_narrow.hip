@@ -19,6 +19,12 @@ namespace {
 // O^T += V^T P^T with MFMA 16x16x16 whose V^T operand comes from
 // ds_read_b64_tr_b16.  The waves' (max, sum, O) states are merged through
 // LDS at the end of the item.
+// Groups of 33-64 rows on pages of at least 16 tokens (RH = 2): eight waves,
+// two row halves of 32 rows over the same keys.  The two waves of a key
+// slice each load half of it into one shared ring, so each tile waits on
+// both (its own vmcnt, then one barrier per tile) and the ring, as deep as
+// the LDS holds with one workgroup per CU, keeps more of the cache in flight
+// than two 32-row workgroups that each read every tile.
 namespace narrow {
 
 constexpr int NW = 4;    // waves per workgroup
@@ -225,13 +231,30 @@ struct SliceDMA {
                                        kStreamPolicy);
     }
   }
+  // the same for a wave that shares the slice with another: loads
+  // 2 k + h (h = 0, 1) only; the per-load values are selected, not indexed,
+  // so they stay in registers
+  __device__ __forceinline__ void issue_clamped_half(char* dst, const char* base, int valid,
+                                                     int64_t token_stride, int h) const {
+    static_assert(N % 2 == 0, "two equal parts");
+#pragma unroll
+    for (int k = 0; k < N / 2; ++k) {
+      const int rw = h ? row[2 * k + 1] : row[2 * k];
+      const uint32_t o = h ? off[2 * k + 1] : off[2 * k];
+      const int r = min(rw, valid - 1);
+      const char* src = base + o + (int64_t)(r - rw) * token_stride * 2;
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(dst + (2 * k + h) * 1024),
+                                       16, 0, kStreamPolicy);
+    }
+  }
 };
 
-template <int KIND, int D, int DR, int RT, int STAGES, bool SP>
+template <int KIND, int D, int DR, int RT, int STAGES, bool SP, int RH>
 // Two workgroups (two waves per SIMD) share a CU up to two row tiles per
 // wave: with two, the register budget is held to that (one row tile fits
-// without asking; four: one wave per SIMD).
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RT == 2 ? 2 : 1)))
+// without asking; four: one wave per SIMD).  RH = 2: one workgroup of
+// eight waves, two row halves over the same keys (two waves per SIMD).
+__global__ __launch_bounds__(NW * RH * 64) __attribute__((amdgpu_waves_per_eu(RT == 2 ? 2 : 1)))
 void decode_narrow(Params p) {
   using G = Geo<KIND, D, DR>;
   constexpr bool TIED = KIND != GQA;   // tied state + one RoPE key head
@@ -243,6 +266,9 @@ void decode_narrow(Params p) {
   constexpr int CPRR = (DR > 0) ? G::ROWR / 16 : 1;
   static_assert(STAGES >= 2 && STAGES <= 6, "stages");
   static_assert(G::LOADS * 1024 == G::WAVE_BYTES, "whole 1 KB load instructions");
+  static_assert(RH == 1 || (RH == 2 && !SP && !PAIR), "row halves: whole slices, one group");
+  // cache loads per tile of one wave (+ the page-id load of small pages)
+  constexpr int LW = G::LOADS / RH + (SP ? 1 : 0);
 
   __shared__ __attribute__((aligned(1024))) char st0[G::STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) char st1[G::STAGE_BYTES];
@@ -250,7 +276,7 @@ void decode_narrow(Params p) {
   __shared__ __attribute__((aligned(1024))) char st3[STAGES > 3 ? G::STAGE_BYTES : 16];
   __shared__ __attribute__((aligned(1024))) char st4[STAGES > 4 ? G::STAGE_BYTES : 16];
   __shared__ __attribute__((aligned(1024))) char st5[STAGES > 5 ? G::STAGE_BYTES : 16];
-  __shared__ float merge_m[NW][16 * RT], merge_l[NW][16 * RT];
+  __shared__ float merge_m[RH][NW][16 * RT], merge_l[RH][NW][16 * RT];
   __shared__ int merge_last;
   // pages smaller than a slice (SP): page ids of each wave's 16 keys of a
   // tile, in a ring of STAGES + 1 slots, loaded STAGES tiles ahead
@@ -259,7 +285,9 @@ void decode_narrow(Params p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // key wave (keys [16 wave, 16 wave + 16) of every tile) and row half
+  const int wave = __builtin_amdgcn_readfirstlane(RH == 1 ? tid >> 6 : (tid >> 6) % NW);
+  const int half = RH == 1 ? 0 : __builtin_amdgcn_readfirstlane((tid >> 6) / NW);
   const int col = lane & 15;
   const int grp = lane >> 4;
 
@@ -270,8 +298,9 @@ void decode_narrow(Params p) {
   // With a work queue (GQA) the grid holds as many workgroups as the GPU
   // keeps resident: block i takes item i first, and later items go to the
   // workgroups that finish first, whatever their XCD.  Groups of more than
-  // 32 rows split into nrb workgroups of 32 rows (row block rblk), which
-  // run on the same XCD: the second reads the item's cache rows from its L2.
+  // 32 rows without row halves split into nrb workgroups of 32 rows (row
+  // block rblk), which run on the same XCD: the second reads the item's
+  // cache rows from its L2.
   const int gsz = p.row_blocks;  // items per unit kept on one XCD
   const int nrb = p.nrb;         // workgroups per item
   const int bid = blockIdx.x;
@@ -311,13 +340,13 @@ void decode_narrow(Params p) {
   const int pmask = (1 << p.page_shift) - 1;
   const int32_t* pt_row = p.page_table + (int64_t)b * p.max_pages;
 
-  // rows of this lane (every wave holds every row); GTA2: rows
+  // rows of this lane (every wave of a row half holds all of its rows); GTA2: rows
   // [0, p.rows) belong to group j, rows [p.rows, 2 p.rows) to group j + 1
   int tq[RT], hq[RT], qlimit[RT];
   bool row_ok[RT], row_b[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    const int row = rblk * 16 * RT + rt * 16 + col;
+    const int row = ((rblk * RH + half) * RT + rt) * 16 + col;
     row_ok[rt] = row < (PAIR ? 2 : 1) * p.rows;
     row_b[rt] = PAIR && row >= p.rows;
     const int rr = row_b[rt] ? row - p.rows : row;
@@ -389,14 +418,22 @@ void decode_narrow(Params p) {
     // rows past the chunk's end re-read its last row (for a slice wholly
     // past the end, kc is that row and slot0 its 16-aligned block)
     const int v = min((key0 <= t_last) ? valid : ((kc & pmask) - slot0 + 1), KW);
-    dma0.issue_clamped(dst + G::K_OFF, b0, v, p.token_stride);
+    // row halves: the two waves of a slice issue alternate loads of it
+    auto part = [&](const auto& dma, char* d, const char* base, int64_t ts) {
+      if constexpr (RH == 1) {
+        dma.issue_clamped(d, base, v, ts);
+      } else {
+        dma.issue_clamped_half(d, base, v, ts, half);
+      }
+    };
+    part(dma0, dst + G::K_OFF, b0, p.token_stride);
     if constexpr (PAIR) dma0.issue_clamped(dst + G::K2_OFF, b0 + p.head_stride * 2, v, p.token_stride);
     if constexpr (KIND == GQA) {
-      dma0.issue_clamped(dst + G::V_OFF, p.pool1 + row0 * 2, v, p.token_stride);
+      part(dma0, dst + G::V_OFF, p.pool1 + row0 * 2, p.token_stride);
     } else {
-      dmar.issue_clamped(dst + G::R_OFF,
-                         p.rope + (page * p.rpage_stride + (int64_t)slot0 * p.rtoken_stride) * 2,
-                         v, p.rtoken_stride);
+      part(dmar, dst + G::R_OFF,
+           p.rope + (page * p.rpage_stride + (int64_t)slot0 * p.rtoken_stride) * 2,
+           p.rtoken_stride);
     }
   };
 
@@ -469,7 +506,7 @@ void decode_narrow(Params p) {
     for (int u = 0; u < STAGES - 1; ++u) issue(u, u);
   }
   {
-    constexpr int ahead = (STAGES - 1) * (G::LOADS + (SP ? 1 : 0));
+    constexpr int ahead = (STAGES - 1) * LW;
     __builtin_amdgcn_s_waitcnt((ahead & 15) | ((ahead >> 4) << 14) | (0x7 << 4) | (0xf << 8));
   }
 
@@ -511,7 +548,10 @@ void decode_narrow(Params p) {
     u32x4_t kraw[NKC];
     u64_t vraw[NDVT];
     {
-      const uint32_t sbase = lds_addr(sb);
+      uint32_t sbase = lds_addr(sb);
+      // row halves (eight waves, a deeper ring, 256 registers): operand
+      // addresses are formed per slice rather than kept for every stage
+      if constexpr (RH == 2) asm volatile("" : "+s"(sbase));
       const uint32_t vbase = sbase + ((KIND == GQA) ? G::V_OFF : G::K_OFF);
       uint32_t ka_addr[NKC], va_addr[NDVT];
 #pragma unroll
@@ -702,12 +742,22 @@ void decode_narrow(Params p) {
 #pragma unroll
     for (int u = 0; u < STAGES; ++u) {
       if (t + u < n_tiles) {
-        // every wave has read stage (u-1) of the previous tile before reuse
-        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-        issue(t + u + STAGES - 1, (u + STAGES - 1) % STAGES);
-        // wait until this tile's loads (issued STAGES-1 tiles ago) landed
-        constexpr int ahead = (STAGES - 1) * (G::LOADS + (SP ? 1 : 0));
-        __builtin_amdgcn_s_waitcnt((ahead & 15) | ((ahead >> 4) << 14) | (0x7 << 4) | (0xf << 8));
+        if constexpr (RH == 1) {
+          // every wave has read stage (u-1) of the previous tile before reuse
+          __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+          issue(t + u + STAGES - 1, (u + STAGES - 1) % STAGES);
+          // wait until this tile's loads (issued STAGES-1 tiles ago) landed
+          constexpr int ahead = (STAGES - 1) * LW;
+          __builtin_amdgcn_s_waitcnt((ahead & 15) | ((ahead >> 4) << 14) | (0x7 << 4) | (0xf << 8));
+        } else {
+          // row halves: this wave's part of tile t + u has landed; after the
+          // barrier both parts have, and both halves are done with tile
+          // t + u - 1, whose stage then takes tile t + u + STAGES - 1
+          constexpr int ahead = (STAGES - 2) * LW;
+          __builtin_amdgcn_s_waitcnt((ahead & 15) | ((ahead >> 4) << 14) | (0x7 << 4) | (0xf << 8));
+          __syncthreads();
+          issue(t + u + STAGES - 1, (u + STAGES - 1) % STAGES);
+        }
         // the next item's ticket, drawn as the last tile starts so that the
         // atomic's round trip overlaps this tile's arithmetic
         if (p.queue && t + u == n_tiles - 1 && tid == 0)
@@ -724,27 +774,27 @@ void decode_narrow(Params p) {
   for (int rt = 0; rt < RT; ++rt) {
     const float l_w = wave_sum4(l_run[rt]);
     if (grp == 0) {
-      merge_m[wave][rt * 16 + col] = m_run[rt];
-      merge_l[wave][rt * 16 + col] = l_w;
+      merge_m[half][wave][rt * 16 + col] = m_run[rt];
+      merge_l[half][wave][rt * 16 + col] = l_w;
     }
   }
   __syncthreads();
   // columns merged per pass: the largest power of two whose four per-wave
-  // 16-row slabs fit one stage buffer
-  constexpr int DP0 = G::STAGE_BYTES / (NW * 16 * 4);
+  // 16-row slabs (of each row half) fit one stage buffer
+  constexpr int DP0 = G::STAGE_BYTES / (RH * NW * 16 * 4);
   constexpr int DP = DP0 >= D ? D : DP0 >= 128 ? 128 : DP0 >= 64 ? 64 : 32;
   static_assert(D % DP == 0 && DP % (NW * 4) == 0, "merge passes");
-  float* obuf = reinterpret_cast<float*>(st0);  // [NW][16][DP] fp32
+  float* obuf = reinterpret_cast<float*>(st0) + half * (NW * 16 * DP);  // [NW][16][DP] fp32
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int r = rt * 16 + col;
     float mx = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, merge_m[w][r]);
+    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, merge_m[half][w][r]);
     const float mu = (mx == -INFINITY) ? 0.f : mx;
     float lt = 0.f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) lt += merge_l[w][r] * exp2f(merge_m[w][r] - mu);
+    for (int w = 0; w < NW; ++w) lt += merge_l[half][w][r] * exp2f(merge_m[half][w][r] - mu);
     const float sc = exp2f(m_run[rt] - mu);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     const float lse_val = lt > 0.f ? (mu + __log2f(lt)) * 0.69314718055994531f : -INFINITY;
@@ -796,7 +846,8 @@ void decode_narrow(Params p) {
 #pragma unroll
     for (int jj = j; jj < j + (PAIR ? 2 : 1); ++jj)
       arrive_and_merge<D>(p, p.counters + ((int64_t)b * (p.h_q / p.g) + jj) * nrb + rblk,
-                          &merge_last, b, jj, rblk * 16 * RT, min(16 * RT, p.rows - rblk * 16 * RT),
+                          &merge_last, b, jj, rblk * 16 * RT * RH,
+                          min(16 * RT * RH, p.rows - rblk * 16 * RT * RH),
                           n_splits, slot_base);
   }
 
@@ -819,11 +870,11 @@ void decode_narrow(Params p) {
 
 }  // namespace narrow
 
-template <int KIND, int D, int DR, int RT, int S, bool SP = false>
+template <int KIND, int D, int DR, int RT, int S, bool SP = false, int RH = 1>
 int launch_narrow_s(Params p, int n_items, int groups, hipStream_t stream) {
   using G = narrow::Geo<KIND, D, DR>;
   if constexpr (S * G::STAGE_BYTES + 4096 > 163840) {
-    return launch_narrow_s<KIND, D, DR, RT, S - 1, SP>(p, n_items, groups, stream);
+    return launch_narrow_s<KIND, D, DR, RT, S - 1, SP, RH>(p, n_items, groups, stream);
   } else {
     p.n_items = n_items;
     // GTA: the groups of one (sequence, chunk) share an XCD (its L2 serves
@@ -832,7 +883,7 @@ int launch_narrow_s(Params p, int n_items, int groups, hipStream_t stream) {
     // GTA2: a unit is a pair of plan items (two groups)
     const int gsz = KIND == GTA ? groups : KIND == GTA2 ? groups / 2 : 1;
     const int units = KIND == GTA2 ? n_items / 2 : n_items;
-    const int nrb = (p.rows + 16 * RT - 1) / (16 * RT);  // workgroups per item
+    const int nrb = (p.rows + 16 * RT * RH - 1) / (16 * RT * RH);  // workgroups per item
     p.row_blocks = gsz;
     p.nrb = nrb;
     int blocks = (units + 8 * gsz - 1) / (8 * gsz) * 8 * gsz * nrb;
@@ -841,16 +892,21 @@ int launch_narrow_s(Params p, int n_items, int groups, hipStream_t stream) {
     } else {
       p.queue = nullptr;
     }
-    hipLaunchKernelGGL((narrow::decode_narrow<KIND, D, DR, RT, S, SP>), dim3(blocks),
-                       dim3(narrow::NW * 64), 0, stream, p);
+    hipLaunchKernelGGL((narrow::decode_narrow<KIND, D, DR, RT, S, SP, RH>), dim3(blocks),
+                       dim3(narrow::NW * RH * 64), 0, stream, p);
     return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
   }
 }
 
+// pages of fewer than 16 tokens (or forced): per-row page ids
+bool narrow_sp(const Params& p) {
+  return p.page_shift < 4 || attn_internal::env_int("ATTN_FORCE_SP", 0);
+}
+
 template <int KIND, int D, int DR, int RT>
 int launch_narrow_rt(const Params& p, int n_items, int groups, int stages, hipStream_t stream) {
-  // pages of fewer than 16 tokens: per-row page ids, rings of 2 to 4 stages
-  if (p.page_shift < 4 || attn_internal::env_int("ATTN_FORCE_SP", 0)) {
+  // small pages: rings of 2 to 4 stages
+  if (narrow_sp(p)) {
     return stages >= 4   ? launch_narrow_s<KIND, D, DR, RT, 4, true>(p, n_items, groups, stream)
            : stages == 3 ? launch_narrow_s<KIND, D, DR, RT, 3, true>(p, n_items, groups, stream)
                          : launch_narrow_s<KIND, D, DR, RT, 2, true>(p, n_items, groups, stream);
@@ -870,8 +926,21 @@ int launch_narrow(const Params& p, int n_items, int groups, int stages, hipStrea
   if constexpr (KIND == GTA2) return launch_narrow_rt<KIND, D, DR, 1>(p, n_items, groups, stages, stream);
   const int rt = (p.rows + 15) / 16;
   if (rt <= 1) return launch_narrow_rt<KIND, D, DR, 1>(p, n_items, groups, stages, stream);
-  // more than 32 rows: two workgroups of two row tiles (two waves per SIMD),
-  // unless ATTN_NARROW_RT4=1 keeps them in one of four row tiles
+  // more than 32 rows on pages of 16 tokens or more: one workgroup of two
+  // row halves of two row tiles each, over one ring; else two workgroups of
+  // two row tiles (two waves per SIMD either way), unless ATTN_NARROW_RT4=1
+  // keeps them in one of four row tiles
+  if constexpr (KIND != GTA2) {
+    if (rt > 2 && attn_internal::narrow_row_halves(p.page_shift >= 4) && !narrow_sp(p)) {
+      switch (stages) {
+        case 2: return launch_narrow_s<KIND, D, DR, 2, 2, false, 2>(p, n_items, groups, stream);
+        case 3: return launch_narrow_s<KIND, D, DR, 2, 3, false, 2>(p, n_items, groups, stream);
+        case 4: return launch_narrow_s<KIND, D, DR, 2, 4, false, 2>(p, n_items, groups, stream);
+        case 5: return launch_narrow_s<KIND, D, DR, 2, 5, false, 2>(p, n_items, groups, stream);
+        default: return launch_narrow_s<KIND, D, DR, 2, 6, false, 2>(p, n_items, groups, stream);
+      }
+    }
+  }
   if (rt <= 2 || !attn_internal::env_narrow_rt4())
     return launch_narrow_rt<KIND, D, DR, 2>(p, n_items, groups, stages, stream);
   return launch_narrow_rt<KIND, D, DR, 4>(p, n_items, groups, stages, stream);

@@ -66,6 +66,11 @@ SMALL = {
                        seqlen_hi=200, max_seqlen=200),
     "gqa4_q12": small("gqa4_8k", batch=2, q_len=12, causal=True, seqlen_lo=12,
                       seqlen_hi=300, max_seqlen=320),
+    # 64-row groups on whole slices: one workgroup of two row halves
+    "gta_q8": small("gta_8k", batch=2, q_len=8, causal=True, seqlen_lo=8, seqlen_hi=400,
+                    max_seqlen=448),
+    "gqa4_q8_p16": small("gqa4_8k", batch=2, q_len=8, causal=True, page_size=16, seqlen_lo=8,
+                         seqlen_hi=400, max_seqlen=448),
     # latent groups whose rows are no multiple of 16: 24 rows (one partial
     # row tile), 60 (two row tiles, the last partial), 144 (row blocks of
     # 64, 64 and 16), and 3 rows in each of four GLA groups
