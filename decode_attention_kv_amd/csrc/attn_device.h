@@ -174,6 +174,11 @@ __device__ __forceinline__ void dma16v(uint64_t addr, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" : : "v"(addr), "s"(l)
                : "memory");
 }
+__device__ __forceinline__ void dma16v_cached(uint64_t addr, uint32_t lds) {
+  const uint32_t l = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(addr), "s"(l)
+               : "memory");
+}
 __device__ __forceinline__ void dma4(const char* base, uint32_t voff, uint32_t lds) {
   const uint32_t l = __builtin_amdgcn_readfirstlane(lds);
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" : : "v"(voff), "s"(base),

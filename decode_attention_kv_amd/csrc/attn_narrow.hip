@@ -178,8 +178,12 @@ __device__ __forceinline__ constexpr int chunk_swz(int r, int cpr) {
 // row is read once per call, and the hint raises streaming read bandwidth
 // by about a tenth on gfx950.
 constexpr int kStreamPolicy = 2;  // nt
+// The GTA RoPE key rows are shared by every group of a sequence, whose
+// workgroups run on one XCD: loaded with the default policy, so that the
+// groups after the first find them in its L2.
+constexpr int kSharedPolicy = 0;
 
-template <int ROWB>
+template <int ROWB, int POLICY = kStreamPolicy>
 struct SliceDMA {
   static constexpr int CPR = ROWB / 16;  // 16-byte chunks per row
   static constexpr int RPI = 64 / CPR;   // rows per 1 KB load
@@ -211,14 +215,19 @@ struct SliceDMA {
   __device__ __forceinline__ void issue_sp(char* dst, const char* base, const uint64_t* o) const {
     const uint64_t b = reinterpret_cast<uint64_t>(base);
 #pragma unroll
-    for (int i = 0; i < N; ++i) dma16v(b + o[i], lds_u32(dst + i * 1024));
+    for (int i = 0; i < N; ++i) {
+      if constexpr (POLICY == kStreamPolicy)
+        dma16v(b + o[i], lds_u32(dst + i * 1024));
+      else
+        dma16v_cached(b + o[i], lds_u32(dst + i * 1024));
+    }
   }
   // full slice: every row valid, contiguous within one page
   __device__ __forceinline__ void issue(char* dst, const char* base) const {
 #pragma unroll
     for (int i = 0; i < N; ++i)
       __builtin_amdgcn_global_load_lds((const void*)(base + off[i]), (lds_void_t*)(dst + i * 1024),
-                                       16, 0, kStreamPolicy);
+                                       16, 0, POLICY);
   }
   // partial slice: rows at or past `valid` re-read row valid-1 (same page)
   __device__ __forceinline__ void issue_clamped(char* dst, const char* base, int valid,
@@ -228,7 +237,7 @@ struct SliceDMA {
       const int r = min(row[i], valid - 1);
       const char* src = base + off[i] + (int64_t)(r - row[i]) * token_stride * 2;
       __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(dst + i * 1024), 16, 0,
-                                       kStreamPolicy);
+                                       POLICY);
     }
   }
   // the same for a wave that shares the slice with another: loads
@@ -244,7 +253,7 @@ struct SliceDMA {
       const int r = min(rw, valid - 1);
       const char* src = base + o + (int64_t)(r - rw) * token_stride * 2;
       __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(dst + (2 * k + h) * 1024),
-                                       16, 0, kStreamPolicy);
+                                       16, 0, POLICY);
     }
   }
 };
@@ -368,7 +377,7 @@ void decode_narrow(Params p) {
 
   // direct-to-LDS load offsets of this lane (loop invariant)
   SliceDMA<G::ROW0> dma0;
-  SliceDMA<(DR > 0 ? G::ROWR : 16)> dmar;
+  SliceDMA<(DR > 0 ? G::ROWR : 16), kSharedPolicy> dmar;
   dma0.init(p.token_stride, lane);
   if constexpr (TIED) dmar.init(p.rtoken_stride, lane);
 
@@ -398,7 +407,7 @@ void decode_narrow(Params p) {
       if constexpr (KIND == GQA) {
         dma0.issue_sp(dst + G::V_OFF, p.pool1, o);
       } else {
-        uint64_t orr[SliceDMA<(DR > 0 ? G::ROWR : 16)>::N];
+        uint64_t orr[SliceDMA<(DR > 0 ? G::ROWR : 16), kSharedPolicy>::N];
         dmar.offsets_sp(orr, ids, kw, t_last, pmask, p.rpage_stride, p.rtoken_stride, 0);
         dmar.issue_sp(dst + G::R_OFF, p.rope, orr);
       }
