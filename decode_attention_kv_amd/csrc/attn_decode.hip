@@ -89,16 +89,18 @@ bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
 // workgroups of `per_cu` per CU the current device keeps resident
 int resident_slots(int per_cu) {
-  static int cus[64] = {0};
+  // looked up once per device; calls from several host threads may race to
+  // store the same value
+  static std::atomic<int> cus[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cus[dev] == 0) {
-    int n = 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return 0;
-    cus[dev] = n;
+    cus[dev].store(n, std::memory_order_relaxed);
   }
-  return cus[dev] * per_cu;
+  return n * per_cu;
 }
 
 // the plan's device arrays, or a plan to pass in the launch arguments
