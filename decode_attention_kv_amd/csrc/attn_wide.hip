@@ -90,6 +90,14 @@ __device__ __forceinline__ void dma16(const char* base, uint32_t voff, uint32_t 
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt" : : "v"(voff), "s"(base),
                "s"(l) : "memory");
 }
+// The same with the default cache policy, for the RoPE key rows: every
+// latent group of a sequence reads them, on one XCD, so the groups after
+// the first find them in its L2.
+__device__ __forceinline__ void dma16_cached(const char* base, uint32_t voff, uint32_t lds) {
+  const uint32_t l = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(base),
+               "s"(l) : "memory");
+}
 
 
 template <int DC, int DR> struct Geo {
@@ -254,7 +262,7 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
     if (k < LK)
       dma16(f.lbase + (int64_t)blk * RPB * lts2, vlat, f.sbase + blk * G::BSTR);
     else
-      dma16(f.rbase + (int64_t)blk * 8 * rts2, vrope, f.sbase + G::R_OFF + blk * 1024);
+      dma16_cached(f.rbase + (int64_t)blk * 8 * rts2, vrope, f.sbase + G::R_OFF + blk * 1024);
   };
   // a partial last tile: rows past the end re-read the last row, so that
   // stale cache contents never reach the MFMAs
@@ -269,7 +277,7 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
     for (int k = 0; k < RK; ++k) {
       const int blk = wave + NW * k;
       const int r = min(blk * 8 + rrow, f.valid - 1);
-      dma16(f.rbase, (uint32_t)(r * rts2 + runit * 16), f.sbase + G::R_OFF + blk * 1024);
+      dma16_cached(f.rbase, (uint32_t)(r * rts2 + runit * 16), f.sbase + G::R_OFF + blk * 1024);
     }
   };
   // Small pages: every row's address from its own page id (rows past the
@@ -330,7 +338,7 @@ __device__ __forceinline__ bool stream(const Params& p, const Item& itm, char* r
       }
     } else {
       const int kk = k - LK;
-      dma16v(f.ar[kk], f.sbase + G::R_OFF + (wave * RK + kk) * 1024);
+      dma16v_cached(f.ar[kk], f.sbase + G::R_OFF + (wave * RK + kk) * 1024);
     }
   };
 
