@@ -140,7 +140,8 @@ def attn_decode_plan(shape_: Shape, seqlens_host: np.ndarray, cu_count: int, chu
                      items_host: np.ndarray, seqinfo_host: np.ndarray, max_items: int):
     """Returns (status, Plan).  Host numpy arrays, int32, C-contiguous."""
     for a in (seqlens_host, items_host, seqinfo_host):
-        assert a.dtype == np.int32 and a.flags.c_contiguous
+        if a.dtype != np.int32 or not a.flags.c_contiguous:
+            raise ValueError("planner arrays must be C-contiguous int32")
     plan = Plan()
     st = lib().attn_decode_plan(ctypes.byref(shape_), seqlens_host.ctypes.data, cu_count,
                                 chunk_tokens, items_host.ctypes.data, seqinfo_host.ctypes.data,
@@ -231,8 +232,19 @@ def paged_kv(pool0, pool1, rope, page_table, seqlens) -> PagedKV:
     int32 [B].  Works for host tensors too (for attn_paged_kv_check)."""
     import torch
 
-    if pool0.stride(-1) != 1 or (pool1 is not None and pool1.stride(-1) != 1):
-        raise ValueError("pool rows must be contiguous")
+    if pool0.dim() != 4 or pool0.stride(-1) != 1 or (pool1 is not None and pool1.stride(-1) != 1):
+        raise ValueError("pools must be [pages, P, heads, width] with contiguous rows")
+    # the kernels read the page table as int32 rows of max_pages entries and
+    # one int32 length per sequence
+    if (page_table.dtype != torch.int32 or page_table.dim() != 2 or
+            not page_table.is_contiguous()):
+        raise ValueError("page_table must be a contiguous int32 [B, max_pages] tensor")
+    if (seqlens.dtype != torch.int32 or seqlens.dim() != 1 or not seqlens.is_contiguous() or
+            seqlens.shape[0] != page_table.shape[0]):
+        raise ValueError("seqlens must be a contiguous int32 [B] tensor")
+    for t in (pool1, rope, page_table, seqlens):
+        if t is not None and t.device != pool0.device:
+            raise ValueError("the pools, page table and lengths must be on one device")
     # the descriptor holds one set of strides for pool0 and pool1
     if pool1 is not None and (pool1.shape != pool0.shape or pool1.stride() != pool0.stride()):
         raise ValueError("pool1 must have pool0's shape and strides")

@@ -238,6 +238,32 @@ def test_paged_kv_needs_one_layout_for_both_pools():
     assert kv.token_stride == 64 and kv.head_stride == 16 * 64
 
 
+def test_paged_kv_refuses_index_arrays_the_kernels_cannot_read():
+    """The kernels read the page table as contiguous int32 rows and one int32
+    length per sequence: other dtypes, shapes or layouts are refused when
+    the descriptor is built, as are tensors on different devices."""
+    import torch
+
+    k = torch.zeros((4, 16, 2, 64), dtype=torch.bfloat16)
+    table = torch.zeros((2, 3), dtype=torch.int32)
+    seqlens = torch.tensor([5, 9], dtype=torch.int32)
+    binding.paged_kv(k, k, None, table, seqlens)
+    bad = [(table.long(), seqlens), (table.t().contiguous().t(), seqlens), (table[0], seqlens),
+           (table, seqlens.long()), (table, seqlens[:1]), (table, torch.zeros((2, 1), dtype=torch.int32))]
+    for t, l in bad:
+        with pytest.raises(ValueError):
+            binding.paged_kv(k, k, None, t, l)
+    with pytest.raises(ValueError):
+        binding.paged_kv(k[0], k[0], None, table, seqlens)      # not [pages, P, heads, width]
+    with pytest.raises(ValueError):
+        binding.paged_kv(k, k, None, table.to("meta"), seqlens)  # another device
+    with pytest.raises(ValueError):
+        binding.attn_decode_plan(binding.shape("gqa", binding.ATTN_BF16, 2, 1, 8, 2, 64, 0, 16,
+                                               False),
+                                 np.array([5, 9], dtype=np.int64), 256, 0,
+                                 np.zeros((8, 4), np.int32), np.zeros((2, 4), np.int32), 8)
+
+
 def _fake_call(kind="gqa", **over):
     """A decode call with fake (never dereferenced) aligned device pointers:
     validation must reject it before any launch."""
